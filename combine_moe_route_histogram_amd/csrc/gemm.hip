@@ -1,0 +1,146 @@
+// Plain (one launch per GEMM kind) grouped expert-FFN GEMMs and the row-tile
+// planner.  Tile code lives in gemm_tile.hpp.
+//
+// Padding-free grouped GEMM (UniEP article, section 1.2): the rows of expert
+// e are offsets[e]..offsets[e+1] of the expert-contiguous buffer; the row tiles
+// of every group are listed by a one-wave planner straight from the device
+// offsets, so the host never reads a count back.  Tiles never straddle two
+// experts; the last tile of an expert is partial.
+#include "gemm_tile.hpp"
+
+namespace moe {
+
+// Row-tile table: per group (E routed experts, then Ns shared experts over
+// all T tokens) ceil(rows / bm) entries {group, first row, rows, 0}, groups in
+// order; n_mtiles = number of entries.  One wave: each lane owns a contiguous
+// run of groups, a wave scan gives every lane its first table index.
+__global__ __launch_bounds__(64) void plan_mtiles_kernel(const int32_t* __restrict__ offsets, int E,
+                                                         int Ns, int T, int R, int bm,
+                                                         int4* __restrict__ mtiles,
+                                                         int32_t* __restrict__ n_mtiles) {
+  const int lane = threadIdx.x;
+  const int G = E + Ns;
+  const int per = (G + kWave - 1) / kWave;
+  const int g_begin = min(G, lane * per), g_end = min(G, g_begin + per);
+  auto group_rows = [&](int grp, int& row0, int& rows) {
+    if (grp < E) {
+      row0 = offsets[grp];
+      rows = offsets[grp + 1] - row0;
+    } else {
+      row0 = R + (grp - E) * T;
+      rows = T;
+    }
+  };
+  int mine = 0;
+  for (int grp = g_begin; grp < g_end; ++grp) {
+    int row0, rows;
+    group_rows(grp, row0, rows);
+    mine += (rows + bm - 1) / bm;
+  }
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  int idx = incl - mine;
+  for (int grp = g_begin; grp < g_end; ++grp) {
+    int row0, rows;
+    group_rows(grp, row0, rows);
+    for (int r = 0; r < rows; r += bm) mtiles[idx++] = make_int4(grp, row0 + r, min(bm, rows - r), 0);
+  }
+  if (lane == kWave - 1) *n_mtiles = incl;
+}
+
+// Launch order -> logical tile.  Workgroups are handed to the 8 XCDs round
+// robin; remapping gives each XCD a contiguous range of logical tiles, so tiles
+// that share weights (same N-tile, consecutive row tiles) share an L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  if (nblocks % 8) return bid;
+  return (bid % 8) * (nblocks / 8) + bid / 8;
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(GemmArgs g, int mt_count, int nt_count) {
+  extern __shared__ __align__(16) uint16_t smem_bf[];
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  if (L >= mt_count * nt_count) return;
+  const int tm = L % mt_count, tn = L / mt_count;
+  const TileDesc<uint16_t> d = decode_tile<uint16_t, C::KIND, C::BM, C::BN>(g, tm, tn);
+  if (d.skip) return;
+  run_tile_bf16<C>(g, d, smem_bf);
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kF32NT) void gemm_f32_kernel(GemmArgs g, int mt_count, int nt_count) {
+  __shared__ float smem_f[kF32LdsFloats];
+  const int L = blockIdx.x;
+  if (L >= mt_count * nt_count) return;
+  const int tm = L % mt_count, tn = L / mt_count;
+  const TileDesc<float> d = decode_tile<float, KIND, kF32BM, kF32BN>(g, tm, tn);
+  if (d.skip) return;
+  run_tile_f32<KIND>(g, d, smem_f);
+}
+
+// bf16 tile configurations per kind.
+template <int KIND> struct BfPick;
+template <> struct BfPick<kUp> { using C = BfCfg<kUp, 128, 128, 2, 2>; };
+template <> struct BfPick<kDown> { using C = BfCfg<kDown, 128, 128, 2, 2>; };
+template <> struct BfPick<kBwdUp> { using C = BfCfg<kBwdUp, 128, 128, 2, 2>; };
+template <> struct BfPick<kBwdDown> { using C = BfCfg<kBwdDown, 128, 128, 2, 2>; };
+template <> struct BfPick<kWgUp> { using C = BfCfg<kWgUp, 128, 128, 2, 2>; };
+template <> struct BfPick<kWgDown> { using C = BfCfg<kWgDown, 128, 128, 2, 2>; };
+
+template <class C>
+static hipError_t set_lds_limit() {
+  static hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<C>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               C::LDS_BYTES);
+  return once;
+}
+
+template <int KIND>
+static hipError_t launch_kind(bool is_bf16, GemmArgs a, int4* mtiles_ws, int32_t* n_ws,
+                              hipStream_t st) {
+  using C = typename BfPick<KIND>::C;
+  const int BM = is_bf16 ? C::BM : kF32BM;
+  const int BN = is_bf16 ? C::BN : kF32BN;
+  int mt_count;
+  if constexpr (!KindTraits<KIND>::kWgrad) {
+    plan_mtiles_kernel<<<1, 64, 0, st>>>(a.offsets, a.E, a.Ns, a.T, a.R, BM, mtiles_ws, n_ws);
+    a.mtiles = mtiles_ws;
+    a.n_mtiles = n_ws;
+    mt_count = (int)mtile_bound(a.T, a.K, a.E, a.Ns, BM);
+    a.mt_max = mt_count;
+  } else {
+    mt_count = (a.E + a.Ns) * wgrad_mtiles<KIND>(a.H, a.I, BM);
+  }
+  const int nt_count = gemm_ntiles<KIND>(a.H, a.I, BN);
+  const int64_t tiles = (int64_t)mt_count * nt_count;
+  if (tiles <= 0) return hipSuccess;
+  if (tiles > INT_MAX - 8) return hipErrorInvalidValue;
+  if (is_bf16) {
+    hipError_t e = set_lds_limit<C>();
+    if (e != hipSuccess) return e;
+    const int grid = (int)((tiles + 7) / 8 * 8);
+    gemm_bf16_kernel<C><<<grid, C::NT, C::LDS_BYTES, st>>>(a, mt_count, nt_count);
+  } else {
+    gemm_f32_kernel<KIND><<<(int)tiles, kF32NT, 0, st>>>(a, mt_count, nt_count);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(bool is_bf16, int kind, const GemmArgs& a, int4* mtiles_ws,
+                       int32_t* n_mtiles_ws, hipStream_t st) {
+  switch (kind) {
+    case kUp: return launch_kind<kUp>(is_bf16, a, mtiles_ws, n_mtiles_ws, st);
+    case kDown: return launch_kind<kDown>(is_bf16, a, mtiles_ws, n_mtiles_ws, st);
+    case kBwdUp: return launch_kind<kBwdUp>(is_bf16, a, mtiles_ws, n_mtiles_ws, st);
+    case kBwdDown: return launch_kind<kBwdDown>(is_bf16, a, mtiles_ws, n_mtiles_ws, st);
+    case kWgUp: return launch_kind<kWgUp>(is_bf16, a, mtiles_ws, n_mtiles_ws, st);
+    case kWgDown: return launch_kind<kWgDown>(is_bf16, a, mtiles_ws, n_mtiles_ws, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace moe

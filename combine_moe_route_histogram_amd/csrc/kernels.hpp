@@ -1,0 +1,85 @@
+// Host-side launchers of the HIP kernels (internal; the public ABI is moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Tokens per routing chunk: one histogram row and one slot-ranking wave each.
+constexpr int kChunkTokens = 256;
+
+inline int route_nchunk(int T) { return (T + kChunkTokens - 1) / kChunkTokens; }
+
+hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* topk_idx, float* topk_w,
+                        int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* slot_src,
+                        int32_t* chunk_counts, int32_t* chunk_base, hipStream_t st);
+
+// Row kernels; is_bf16 selects the storage type (bf16 or f32).
+hipError_t launch_dispatch(bool is_bf16, const void* x, const int32_t* slot, void* x_perm, int T,
+                           int H, int K, hipStream_t st);
+hipError_t launch_combine(bool is_bf16, const void* y, const int32_t* slot, const float* w,
+                          void* out, int T, int H, int K, int Ns, hipStream_t st);
+hipError_t launch_combine_bwd(bool is_bf16, const void* dout, const void* y, const int32_t* slot,
+                              const float* w, void* dy, float* dw, int T, int H, int K,
+                              hipStream_t st);
+hipError_t launch_dispatch_bwd(bool is_bf16, const void* dx_rows, const int32_t* slot, void* dx,
+                               int T, int H, int K, int Ns, hipStream_t st);
+hipError_t launch_route_bwd(const float* dw, const float* w, const int32_t* idx, float* dl, int T,
+                            int E, int K, hipStream_t st);
+
+// Grouped GEMM kinds of the expert FFN.
+enum GemmKind : int {
+  kUp = 0,       // a|b = X [W1|W3], h = silu(a) b      (forward, first GEMM)
+  kDown = 1,     // y = h W2                            (forward, second GEMM)
+  kBwdUp = 2,    // dh = dY W2^T, SwiGLU backward -> da|db
+  kBwdDown = 3,  // dx = [da db] [W1 W3]^T
+  kWgUp = 4,     // dW1 = X^T da, dW3 = X^T db          (transposed, over rows)
+  kWgDown = 5,   // dW2 = h^T dY
+};
+
+struct GemmArgs {
+  int T, H, E, K, I, Ns, R;
+  const int32_t* offsets;  // [E+1] routed row ranges
+  const int4* mtiles;      // per M-tile {group, first row (all-rows index), rows, 0}
+  const int32_t* n_mtiles; // number of valid entries in mtiles
+  int mt_max;              // host bound on the number of M-tiles
+  const void* x_perm;
+  const void* x;
+  const void* w1;
+  const void* w3;
+  const void* w2;
+  const void* ws1;
+  const void* ws3;
+  const void* ws2;
+  const void* ab;
+  const void* h;
+  const void* dy;
+  const void* dout;
+  const void* dab;
+  void* o_ab;
+  void* o_h;
+  void* o_y;
+  void* o_dab;
+  void* o_dx;
+  float* o_dw1;
+  float* o_dw3;
+  float* o_dw2;
+  float* o_dws1;
+  float* o_dws3;
+  float* o_dws2;
+};
+
+// Upper bound on the number of row tiles of height bm over all groups.
+inline int64_t mtile_bound(int64_t T, int64_t K, int64_t E, int64_t Ns, int bm) {
+  return (T * K + bm - 1) / bm + E + Ns * ((T + bm - 1) / bm);
+}
+
+// Smallest row-tile height used by any GEMM configuration (the f32 tiles are
+// 64 rows); sizes the row-tile tables in the workspace.
+constexpr int kMinTileM = 64;
+
+hipError_t launch_gemm(bool is_bf16, int kind, const GemmArgs& a, int4* mtiles_ws,
+                       int32_t* n_mtiles_ws, hipStream_t st);
+
+}  // namespace moe

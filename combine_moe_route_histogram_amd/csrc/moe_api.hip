@@ -1,0 +1,357 @@
+// C ABI of the MoE expert layer (declared in include/moe.h): argument
+// validation, workspace layout and kernel launches.  No call allocates,
+// frees, copies to the host or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace sections (byte offsets).
+struct Layout {
+  size_t chunk_counts, chunk_base, mtiles, n_mtiles, ready, done, cursor, total;
+};
+
+Layout layout(const moe_dims* d) {
+  Layout L;
+  const size_t nchunk = (size_t)route_nchunk(d->T);
+  const size_t mt = (size_t)mtile_bound(d->T, d->K, d->E, d->n_shared, kMinTileM);
+  size_t off = 0;
+  L.chunk_counts = off; off = align_up(off + nchunk * d->E * 4);
+  L.chunk_base = off;   off = align_up(off + nchunk * d->E * 4);
+  L.mtiles = off;       off = align_up(off + mt * 16);
+  L.n_mtiles = off;     off = align_up(off + 16);
+  L.ready = off;        off = align_up(off + mt * 4);
+  L.done = off;         off = align_up(off + mt * 4);
+  L.cursor = off;       off = align_up(off + 64);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* ws_at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int check_dims(const moe_dims* d) {
+  if (!d) return fail(MOE_EINVAL, "dims is NULL");
+  if (d->T < 1) return fail(MOE_EINVAL, "T must be >= 1 (got %d)", d->T);
+  if (d->E < 1 || d->E > 256) return fail(MOE_EUNSUPPORTED, "E must be in [1, 256] (got %d)", d->E);
+  if (d->K < 1 || d->K > d->E || d->K > 64)
+    return fail(MOE_EUNSUPPORTED, "K must be in [1, min(E, 64)] (got K=%d, E=%d)", d->K, d->E);
+  if (d->H <= 0 || d->H % 64)
+    return fail(MOE_EUNSUPPORTED, "H must be a positive multiple of 64 (got %d)", d->H);
+  if (d->I <= 0 || d->I % 64)
+    return fail(MOE_EUNSUPPORTED, "I must be a positive multiple of 64 (got %d)", d->I);
+  if (d->n_shared < 0 || d->n_shared > 8)
+    return fail(MOE_EUNSUPPORTED, "n_shared must be in [0, 8] (got %d)", d->n_shared);
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16)
+    return fail(MOE_EUNSUPPORTED, "dtype must be MOE_F32 or MOE_BF16 (got %d)", d->dtype);
+  const int64_t ra = (int64_t)d->T * d->K + (int64_t)d->n_shared * d->T;
+  if (ra >= (int64_t)1 << 31) return fail(MOE_EUNSUPPORTED, "R + n_shared*T must be < 2^31");
+  return MOE_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(MOE_EINVAL, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) % 16) return fail(MOE_EINVAL, "%s is not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+int check_ws(const moe_dims* d, const void* ws, size_t ws_bytes) {
+  const size_t need = layout(d).total;
+  if (!ws) return fail(MOE_EWORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return fail(MOE_EWORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  if (ws_bytes < need) return fail(MOE_EWORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, need);
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)            \
+  do {                           \
+    const int _s = (expr);       \
+    if (_s != MOE_OK) return _s; \
+  } while (0)
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+GemmArgs base_args(const moe_dims* d, const int32_t* offsets) {
+  GemmArgs a{};
+  a.T = d->T; a.H = d->H; a.E = d->E; a.K = d->K; a.I = d->I; a.Ns = d->n_shared;
+  a.R = d->T * d->K;
+  a.offsets = offsets;
+  return a;
+}
+
+int gemm(const moe_dims* d, int kind, const GemmArgs& a, void* ws, hipStream_t st, const char* what) {
+  const Layout L = layout(d);
+  return hip_status(launch_gemm(d->dtype == MOE_BF16, kind, a, ws_at<int4>(ws, L.mtiles),
+                                ws_at<int32_t>(ws, L.n_mtiles), st),
+                    what);
+}
+
+struct DeviceCache {
+  std::mutex mu;
+  int cu_count[64] = {0};
+};
+DeviceCache g_dev;
+
+}  // namespace
+
+extern "C" {
+
+int moe_init(int device) {
+  if (device < 0 || device >= 64) return fail(MOE_EINVAL, "device index %d out of range", device);
+  std::lock_guard<std::mutex> lk(g_dev.mu);
+  if (g_dev.cu_count[device]) return MOE_OK;
+  hipDeviceProp_t p;
+  MOE_TRY(hip_status(hipGetDeviceProperties(&p, device), "hipGetDeviceProperties"));
+  g_dev.cu_count[device] = p.multiProcessorCount;
+  return MOE_OK;
+}
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE";
+    case MOE_EHIP: return "MOE_EHIP";
+    default: return "MOE_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+size_t moe_workspace_bytes(const moe_dims* d) {
+  if (check_dims(d) != MOE_OK) return 0;
+  return layout(d).total;
+}
+
+int moe_route(const moe_dims* d, const float* logits, int32_t* topk_idx, float* topk_w,
+              int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* slot_src, void* ws,
+              size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_ptr(logits, "logits"));
+  MOE_TRY(check_ptr(topk_idx, "topk_idx"));
+  MOE_TRY(check_ptr(topk_w, "topk_w"));
+  MOE_TRY(check_ptr(counts, "counts"));
+  MOE_TRY(check_ptr(offsets, "offsets"));
+  MOE_TRY(check_ptr(slot, "slot"));
+  MOE_TRY(check_ptr(slot_src, "slot_src"));
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  const Layout L = layout(d);
+  return hip_status(launch_route(logits, d->T, d->E, d->K, topk_idx, topk_w, counts, offsets, slot,
+                                 slot_src, ws_at<int32_t>(ws, L.chunk_counts),
+                                 ws_at<int32_t>(ws, L.chunk_base), as_stream(stream)),
+                    "moe_route");
+}
+
+int moe_dispatch(const moe_dims* d, const void* x, const int32_t* slot, void* x_perm, void* stream) {
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_ptr(x, "x"));
+  MOE_TRY(check_ptr(slot, "slot"));
+  MOE_TRY(check_ptr(x_perm, "x_perm"));
+  return hip_status(launch_dispatch(d->dtype == MOE_BF16, x, slot, x_perm, d->T, d->H, d->K,
+                                    as_stream(stream)),
+                    "moe_dispatch");
+}
+
+int moe_expert_ffn_up(const moe_dims* d, const void* x_perm, const void* x, const int32_t* offsets,
+                      const void* w1, const void* w3, const void* ws1, const void* ws3, void* ab,
+                      void* h, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_ptr(x_perm, "x_perm"));
+  MOE_TRY(check_ptr(offsets, "offsets"));
+  MOE_TRY(check_ptr(w1, "w1"));
+  MOE_TRY(check_ptr(w3, "w3"));
+  MOE_TRY(check_ptr(ab, "ab"));
+  MOE_TRY(check_ptr(h, "h"));
+  if (d->n_shared) {
+    MOE_TRY(check_ptr(x, "x"));
+    MOE_TRY(check_ptr(ws1, "ws1"));
+    MOE_TRY(check_ptr(ws3, "ws3"));
+  }
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  GemmArgs a = base_args(d, offsets);
+  a.x_perm = x_perm; a.x = x; a.w1 = w1; a.w3 = w3; a.ws1 = ws1; a.ws3 = ws3;
+  a.o_ab = ab; a.o_h = h;
+  return gemm(d, kUp, a, ws, as_stream(stream), "moe_expert_ffn_up");
+}
+
+int moe_expert_ffn_down(const moe_dims* d, const void* h, const int32_t* offsets, const void* w2,
+                        const void* ws2, void* y, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_ptr(h, "h"));
+  MOE_TRY(check_ptr(offsets, "offsets"));
+  MOE_TRY(check_ptr(w2, "w2"));
+  MOE_TRY(check_ptr(y, "y"));
+  if (d->n_shared) MOE_TRY(check_ptr(ws2, "ws2"));
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  GemmArgs a = base_args(d, offsets);
+  a.h = h; a.w2 = w2; a.ws2 = ws2; a.o_y = y;
+  return gemm(d, kDown, a, ws, as_stream(stream), "moe_expert_ffn_down");
+}
+
+int moe_expert_ffn(const moe_dims* d, const void* x_perm, const void* x, const int32_t* offsets,
+                   const void* w1, const void* w3, const void* w2, const void* ws1,
+                   const void* ws3, const void* ws2, void* ab, void* h, void* y, void* ws,
+                   size_t ws_bytes, void* stream) {
+  MOE_TRY(moe_expert_ffn_up(d, x_perm, x, offsets, w1, w3, ws1, ws3, ab, h, ws, ws_bytes, stream));
+  return moe_expert_ffn_down(d, h, offsets, w2, ws2, y, ws, ws_bytes, stream);
+}
+
+int moe_combine(const moe_dims* d, const void* y, const int32_t* slot, const float* topk_w,
+                void* out, void* stream) {
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_ptr(y, "y"));
+  MOE_TRY(check_ptr(slot, "slot"));
+  MOE_TRY(check_ptr(topk_w, "topk_w"));
+  MOE_TRY(check_ptr(out, "out"));
+  return hip_status(launch_combine(d->dtype == MOE_BF16, y, slot, topk_w, out, d->T, d->H, d->K,
+                                   d->n_shared, as_stream(stream)),
+                    "moe_combine");
+}
+
+int moe_dispatch_ffn(const moe_dims* d, const void* x, const int32_t* slot_src,
+                     const int32_t* offsets, const void* w1, const void* w3, const void* ws1,
+                     const void* ws3, void* x_perm, void* ab, void* h, void* ws, size_t ws_bytes,
+                     void* stream) {
+  (void)d; (void)x; (void)slot_src; (void)offsets; (void)w1; (void)w3; (void)ws1; (void)ws3;
+  (void)x_perm; (void)ab; (void)h; (void)ws; (void)ws_bytes; (void)stream;
+  return fail(MOE_EUNSUPPORTED, "moe_dispatch_ffn: not built yet");
+}
+
+int moe_ffn_combine(const moe_dims* d, const void* h, const int32_t* offsets, const void* w2,
+                    const void* ws2, const int32_t* slot, const float* topk_w, void* y, void* out,
+                    void* ws, size_t ws_bytes, void* stream) {
+  (void)d; (void)h; (void)offsets; (void)w2; (void)ws2; (void)slot; (void)topk_w; (void)y;
+  (void)out; (void)ws; (void)ws_bytes; (void)stream;
+  return fail(MOE_EUNSUPPORTED, "moe_ffn_combine: not built yet");
+}
+
+int moe_combine_bwd(const moe_dims* d, const void* dout, const void* y, const int32_t* slot,
+                    const float* topk_w, void* dy, float* dtopk_w, void* stream) {
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_ptr(dout, "dout"));
+  MOE_TRY(check_ptr(y, "y"));
+  MOE_TRY(check_ptr(slot, "slot"));
+  MOE_TRY(check_ptr(topk_w, "topk_w"));
+  MOE_TRY(check_ptr(dy, "dy"));
+  MOE_TRY(check_ptr(dtopk_w, "dtopk_w"));
+  return hip_status(launch_combine_bwd(d->dtype == MOE_BF16, dout, y, slot, topk_w, dy, dtopk_w,
+                                       d->T, d->H, d->K, as_stream(stream)),
+                    "moe_combine_bwd");
+}
+
+int moe_expert_ffn_bwd_data(const moe_dims* d, const void* dy, const void* dout,
+                            const int32_t* offsets, const void* w1, const void* w3,
+                            const void* w2, const void* ws1, const void* ws3, const void* ws2,
+                            const void* ab, void* dab, void* dx_rows, void* ws, size_t ws_bytes,
+                            void* stream) {
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_ptr(dy, "dy"));
+  MOE_TRY(check_ptr(offsets, "offsets"));
+  MOE_TRY(check_ptr(w1, "w1"));
+  MOE_TRY(check_ptr(w3, "w3"));
+  MOE_TRY(check_ptr(w2, "w2"));
+  MOE_TRY(check_ptr(ab, "ab"));
+  MOE_TRY(check_ptr(dab, "dab"));
+  MOE_TRY(check_ptr(dx_rows, "dx_rows"));
+  if (d->n_shared) {
+    MOE_TRY(check_ptr(dout, "dout"));
+    MOE_TRY(check_ptr(ws1, "ws1"));
+    MOE_TRY(check_ptr(ws3, "ws3"));
+    MOE_TRY(check_ptr(ws2, "ws2"));
+  }
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  const hipStream_t st = as_stream(stream);
+  GemmArgs a = base_args(d, offsets);
+  a.dy = dy; a.dout = dout; a.w1 = w1; a.w3 = w3; a.w2 = w2; a.ws1 = ws1; a.ws3 = ws3; a.ws2 = ws2;
+  a.ab = ab; a.o_dab = dab; a.dab = dab; a.o_dx = dx_rows;
+  MOE_TRY(gemm(d, kBwdUp, a, ws, st, "moe_expert_ffn_bwd_data (dh)"));
+  return gemm(d, kBwdDown, a, ws, st, "moe_expert_ffn_bwd_data (dx)");
+}
+
+int moe_expert_ffn_bwd_weight(const moe_dims* d, const void* x_perm, const void* x,
+                              const void* h, const void* dy, const void* dout, const void* dab,
+                              const int32_t* offsets, float* dw1, float* dw3, float* dw2,
+                              float* dws1, float* dws3, float* dws2, void* ws, size_t ws_bytes,
+                              void* stream) {
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_ptr(x_perm, "x_perm"));
+  MOE_TRY(check_ptr(h, "h"));
+  MOE_TRY(check_ptr(dy, "dy"));
+  MOE_TRY(check_ptr(dab, "dab"));
+  MOE_TRY(check_ptr(offsets, "offsets"));
+  MOE_TRY(check_ptr(dw1, "dw1"));
+  MOE_TRY(check_ptr(dw3, "dw3"));
+  MOE_TRY(check_ptr(dw2, "dw2"));
+  if (d->n_shared) {
+    MOE_TRY(check_ptr(x, "x"));
+    MOE_TRY(check_ptr(dout, "dout"));
+    MOE_TRY(check_ptr(dws1, "dws1"));
+    MOE_TRY(check_ptr(dws3, "dws3"));
+    MOE_TRY(check_ptr(dws2, "dws2"));
+  }
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  const hipStream_t st = as_stream(stream);
+  GemmArgs a = base_args(d, offsets);
+  a.x_perm = x_perm; a.x = x; a.h = h; a.dy = dy; a.dout = dout; a.dab = dab;
+  a.o_dw1 = dw1; a.o_dw3 = dw3; a.o_dw2 = dw2; a.o_dws1 = dws1; a.o_dws3 = dws3; a.o_dws2 = dws2;
+  MOE_TRY(gemm(d, kWgUp, a, ws, st, "moe_expert_ffn_bwd_weight (dW1, dW3)"));
+  return gemm(d, kWgDown, a, ws, st, "moe_expert_ffn_bwd_weight (dW2)");
+}
+
+int moe_dispatch_bwd(const moe_dims* d, const void* dx_rows, const int32_t* slot, void* dx,
+                     void* stream) {
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_ptr(dx_rows, "dx_rows"));
+  MOE_TRY(check_ptr(slot, "slot"));
+  MOE_TRY(check_ptr(dx, "dx"));
+  return hip_status(launch_dispatch_bwd(d->dtype == MOE_BF16, dx_rows, slot, dx, d->T, d->H, d->K,
+                                        d->n_shared, as_stream(stream)),
+                    "moe_dispatch_bwd");
+}
+
+int moe_route_bwd(const moe_dims* d, const float* dtopk_w, const float* topk_w,
+                  const int32_t* topk_idx, float* dlogits, void* stream) {
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_ptr(dtopk_w, "dtopk_w"));
+  MOE_TRY(check_ptr(topk_w, "topk_w"));
+  MOE_TRY(check_ptr(topk_idx, "topk_idx"));
+  MOE_TRY(check_ptr(dlogits, "dlogits"));
+  return hip_status(launch_route_bwd(dtopk_w, topk_w, topk_idx, dlogits, d->T, d->E, d->K,
+                                     as_stream(stream)),
+                    "moe_route_bwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,219 @@
+// Routing: gate top-k with a fixed tie-break, softmax over the selected
+// logits, per-expert histogram, and the deterministic (token, k) -> slot map.
+//
+// UniEP article, section 1.1 (gate scores, top-k per token) and section 2.2,
+// "deterministic token mapping" / Algorithm 1: a stable sort by expert, the
+// per-expert counts and prefix-sum base offsets give each pair a unique slot
+// without atomic locks.  On one GPU the "ranks" of Algorithm 1 become chunks
+// of 256 tokens: the base of chunk c in expert e is the sum of the counts of
+// lower chunks for e (exactly the rank-major prefix of the article), and the
+// position inside a chunk is the pair's rank among the chunk's pairs routed to
+// e, taken with wave ballots in (token, k) order.  No atomic decides a slot.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+// Order-preserving 64-bit key: a larger logit gives a larger key; for equal
+// logits the lower expert id gives the larger key.  -0.0 is folded onto +0.0.
+__device__ __forceinline__ uint64_t route_key(float l, int e) {
+  uint32_t u = __float_as_uint(l);
+  if ((u << 1) == 0u) u = 0u;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+__device__ __forceinline__ float route_key_logit(uint64_t key) {
+  const uint32_t hi = (uint32_t)(key >> 32);
+  return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// One group of G lanes per token (G = min(64, next pow2 >= E)); each lane owns
+// up to 4 experts (e = lane + i*G).  K rounds of a group-wide max over the
+// keys pick the experts in descending order.  Block = 256 threads = 4 waves,
+// one block per chunk of kChunkTokens tokens; the chunk's expert histogram is
+// accumulated in LDS (integer adds, order-free) and written to chunk_counts.
+template <int G>
+__global__ __launch_bounds__(256) void route_topk_hist_kernel(const float* __restrict__ logits,
+                                                              int T, int E, int K,
+                                                              int32_t* __restrict__ topk_idx,
+                                                              float* __restrict__ topk_w,
+                                                              int32_t* __restrict__ chunk_counts) {
+  __shared__ int hist[256];
+  const int c = blockIdx.x;
+  for (int i = threadIdx.x; i < E; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  constexpr int TPW = kWave / G;  // tokens per wave
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int gl = lane & (G - 1), grp = lane / G;
+  const int t_begin = c * kChunkTokens;
+  const int t_end = min(T, t_begin + kChunkTokens);
+  for (int tb = t_begin + wave * TPW; tb < t_end; tb += 4 * TPW) {
+    const int t = tb + grp;
+    const bool valid = t < t_end;
+    uint64_t key[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = gl + i * G;
+      key[i] = (valid && e < E) ? route_key(logits[(int64_t)t * E + e], e) : 0ull;
+    }
+    float l0 = 0.f, zsum = 0.f, my_l = 0.f;
+    int my_e = 0;
+    for (int k = 0; k < K; ++k) {
+      uint64_t best = umax64(umax64(key[0], key[1]), umax64(key[2], key[3]));
+#pragma unroll
+      for (int o = G / 2; o >= 1; o >>= 1) {
+        const uint64_t other = __shfl_xor(best, o, kWave);
+        best = umax64(best, other);
+      }
+      const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+      const float l = route_key_logit(best);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (e == gl + i * G) key[i] = 0ull;  // an expert is picked once
+      if (k == 0) l0 = l;
+      zsum += expf(l - l0);
+      if (gl == k) {
+        my_l = l;
+        my_e = e;
+      }
+    }
+    if (valid && gl < K) {
+      topk_idx[(int64_t)t * K + gl] = my_e;
+      topk_w[(int64_t)t * K + gl] = expf(my_l - l0) / zsum;
+      atomicAdd(&hist[my_e], 1);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < E; i += blockDim.x) chunk_counts[(int64_t)c * E + i] = hist[i];
+}
+
+// One block per expert: exclusive scan of the expert's column of chunk counts
+// (chunk_base[c][e] = pairs of lower chunks routed to e) and its total.
+__global__ __launch_bounds__(256) void route_chunk_scan_kernel(const int32_t* __restrict__ chunk_counts,
+                                                               int nchunk, int E,
+                                                               int32_t* __restrict__ chunk_base,
+                                                               int32_t* __restrict__ counts) {
+  __shared__ int buf[256];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  int carry = 0;
+  for (int base = 0; base < nchunk; base += 256) {
+    const int c = base + tid;
+    const int v = c < nchunk ? chunk_counts[(int64_t)c * E + e] : 0;
+    buf[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int add = tid >= off ? buf[tid - off] : 0;
+      __syncthreads();
+      buf[tid] += add;
+      __syncthreads();
+    }
+    if (c < nchunk) chunk_base[(int64_t)c * E + e] = carry + buf[tid] - v;
+    carry += buf[255];
+    __syncthreads();
+  }
+  if (tid == 0) counts[e] = carry;
+}
+
+// One wave per chunk.  Expert start offsets = exclusive scan of counts (every
+// wave recomputes it; chunk 0 publishes offsets).  Then the chunk's pairs are
+// taken 64 at a time in (token, k) order: the lanes holding the same expert
+// are found with one ballot per bit of the expert id, a lane's rank among
+// them is the popcount of lower peers, and the highest peer advances the
+// expert's running cursor.  slot = offsets[e] + chunk_base[c][e] + rank.
+__global__ __launch_bounds__(64) void route_slot_kernel(const int32_t* __restrict__ topk_idx,
+                                                        const int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ chunk_base,
+                                                        int T, int E, int K,
+                                                        int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ slot,
+                                                        int32_t* __restrict__ slot_src) {
+  __shared__ int cur[256];
+  const int lane = threadIdx.x, c = blockIdx.x;
+  int v[4], lane_total = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane * 4 + i;
+    v[i] = e < E ? counts[e] : 0;
+    lane_total += v[i];
+  }
+  int incl = lane_total;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  int run = incl - lane_total;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane * 4 + i;
+    if (e < E) {
+      cur[e] = run + chunk_base[(int64_t)c * E + e];
+      if (c == 0) offsets[e] = run;
+    }
+    run += v[i];
+  }
+  if (c == 0 && lane == kWave - 1) offsets[E] = incl;
+  __syncthreads();
+
+  const int t0 = c * kChunkTokens;
+  const int t1 = min(T, t0 + kChunkTokens);
+  const int n = (t1 - t0) * K;
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const uint64_t lower = (1ull << lane) - 1ull;
+  const uint64_t higher = ~((2ull << lane) - 1ull);
+  for (int q0 = 0; q0 < n; q0 += kWave) {
+    const int q = q0 + lane;
+    const bool act = q < n;
+    const int e = act ? topk_idx[(int64_t)t0 * K + q] : 0;
+    uint64_t peers = __ballot(act);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int base = cur[e];
+    __syncthreads();
+    if (act) {
+      const int s = base + __popcll(peers & lower);
+      slot[(int64_t)t0 * K + q] = s;
+      slot_src[s] = t0 + q / K;
+      if ((peers & higher) == 0ull) cur[e] = base + __popcll(peers);
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* topk_idx, float* topk_w,
+                        int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* slot_src,
+                        int32_t* chunk_counts, int32_t* chunk_base, hipStream_t st) {
+  const int nchunk = route_nchunk(T);
+  int g = 1;
+  while (g < E && g < 64) g <<= 1;
+  const dim3 grid(nchunk), block(256);
+  switch (g) {
+#define MOE_ROUTE_CASE(G)                                                                      \
+  case G:                                                                                      \
+    route_topk_hist_kernel<G><<<grid, block, 0, st>>>(logits, T, E, K, topk_idx, topk_w,       \
+                                                      chunk_counts);                           \
+    break;
+    MOE_ROUTE_CASE(1)
+    MOE_ROUTE_CASE(2)
+    MOE_ROUTE_CASE(4)
+    MOE_ROUTE_CASE(8)
+    MOE_ROUTE_CASE(16)
+    MOE_ROUTE_CASE(32)
+    MOE_ROUTE_CASE(64)
+#undef MOE_ROUTE_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  route_chunk_scan_kernel<<<E, 256, 0, st>>>(chunk_counts, nchunk, E, chunk_base, counts);
+  route_slot_kernel<<<nchunk, 64, 0, st>>>(topk_idx, counts, chunk_base, T, E, K, offsets, slot,
+                                           slot_src);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,251 @@
+// Row kernels of the MoE layer: dispatch (permute into expert-contiguous
+// rows), combine (gate-weighted sum back to token order), and the backward of
+// both plus the gate softmax backward.  All are HBM-bound copies/reductions:
+// one wave per token row, 16-byte vector loads and stores, fixed summation
+// order (k = 0..K-1, then shared experts), float32 accumulation.
+//
+// UniEP article, section 1.1: tokens are reordered to their experts
+// (dispatch) and the expert outputs are weighted by the gate scores and summed
+// (combine); the backward mirrors the forward.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kRowBlock = 256;               // 4 waves -> 4 tokens per block
+constexpr int kRowsPerBlock = kRowBlock / kWave;
+
+// x_perm[slot[t,k]] = x[t]: each x row is read once and written K times.
+template <typename S>
+__global__ __launch_bounds__(kRowBlock) void dispatch_kernel(const S* __restrict__ x,
+                                                             const int32_t* __restrict__ slot,
+                                                             S* __restrict__ x_perm, int T, int H,
+                                                             int K) {
+  const int t = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (t >= T) return;
+  const int my_slot = lane < K ? slot[(int64_t)t * K + lane] : 0;
+  const int nvec = H / Elem<S>::kPerVec;
+  const char* src = reinterpret_cast<const char*>(x + (int64_t)t * H);
+  for (int v0 = 0; v0 < nvec; v0 += 4 * kWave) {
+    u32x4 val[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + u * kWave + lane;
+      if (v < nvec) val[u] = ld16(src + (int64_t)v * 16);
+    }
+    for (int k = 0; k < K; ++k) {
+      const int s = __shfl(my_slot, k, kWave);
+      char* dst = reinterpret_cast<char*>(x_perm + (int64_t)s * H);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int v = v0 + u * kWave + lane;
+        if (v < nvec) st16(dst + (int64_t)v * 16, val[u]);
+      }
+    }
+  }
+}
+
+// out[t] = sum_k w[t,k] y[slot[t,k]] + sum_s y[R + s*T + t]; one rounding.
+template <typename S>
+__device__ __forceinline__ void combine_row(const S* __restrict__ y, const int32_t* __restrict__ slot,
+                                            const float* __restrict__ w, S* __restrict__ out,
+                                            int t, int T, int H, int K, int Ns, int lane) {
+  constexpr int P = Elem<S>::kPerVec;
+  const int my_slot = lane < K ? slot[(int64_t)t * K + lane] : 0;
+  const float my_w = lane < K ? w[(int64_t)t * K + lane] : 0.f;
+  const int64_t R = (int64_t)T * K;
+  const int nvec = H / P;
+  for (int v = lane; v < nvec; v += kWave) {
+    float acc[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) acc[j] = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int s = __shfl(my_slot, k, kWave);
+      const float wk = __shfl(my_w, k, kWave);
+      float f[P];
+      Elem<S>::unpack(ld16(reinterpret_cast<const char*>(y + (int64_t)s * H) + (int64_t)v * 16), f);
+#pragma unroll
+      for (int j = 0; j < P; ++j) acc[j] = fmaf(wk, f[j], acc[j]);
+    }
+    for (int sh = 0; sh < Ns; ++sh) {
+      float f[P];
+      Elem<S>::unpack(ld16(reinterpret_cast<const char*>(y + (R + (int64_t)sh * T + t) * H) +
+                           (int64_t)v * 16), f);
+#pragma unroll
+      for (int j = 0; j < P; ++j) acc[j] += f[j];
+    }
+    st16(reinterpret_cast<char*>(out + (int64_t)t * H) + (int64_t)v * 16, Elem<S>::pack(acc));
+  }
+}
+
+template <typename S>
+__global__ __launch_bounds__(kRowBlock) void combine_kernel(const S* __restrict__ y,
+                                                            const int32_t* __restrict__ slot,
+                                                            const float* __restrict__ w,
+                                                            S* __restrict__ out, int T, int H,
+                                                            int K, int Ns) {
+  const int t = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+  if (t >= T) return;
+  combine_row<S>(y, slot, w, out, t, T, H, K, Ns, threadIdx.x & (kWave - 1));
+}
+
+// dy[slot[t,k]] = w[t,k] dout[t];  dw[t,k] = <dout[t], y[slot[t,k]]>.
+// The dot product: per-lane partial sums in vector order, then a fixed
+// butterfly across the wave.
+template <typename S>
+__global__ __launch_bounds__(kRowBlock) void combine_bwd_kernel(const S* __restrict__ dout,
+                                                                const S* __restrict__ y,
+                                                                const int32_t* __restrict__ slot,
+                                                                const float* __restrict__ w,
+                                                                S* __restrict__ dy,
+                                                                float* __restrict__ dw, int T,
+                                                                int H, int K) {
+  constexpr int P = Elem<S>::kPerVec;
+  const int t = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (t >= T) return;
+  const int my_slot = lane < K ? slot[(int64_t)t * K + lane] : 0;
+  const float my_w = lane < K ? w[(int64_t)t * K + lane] : 0.f;
+  const int nvec = H / P;
+  const char* g_row = reinterpret_cast<const char*>(dout + (int64_t)t * H);
+  for (int k = 0; k < K; ++k) {
+    const int s = __shfl(my_slot, k, kWave);
+    const float wk = __shfl(my_w, k, kWave);
+    const char* y_row = reinterpret_cast<const char*>(y + (int64_t)s * H);
+    char* dy_row = reinterpret_cast<char*>(dy + (int64_t)s * H);
+    float part = 0.f;
+    for (int v = lane; v < nvec; v += kWave) {
+      float g[P], f[P], o[P];
+      Elem<S>::unpack(ld16(g_row + (int64_t)v * 16), g);
+      Elem<S>::unpack(ld16(y_row + (int64_t)v * 16), f);
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        part = fmaf(g[j], f[j], part);
+        o[j] = wk * g[j];
+      }
+      st16(dy_row + (int64_t)v * 16, Elem<S>::pack(o));
+    }
+    part = wave_sum(part);
+    if (lane == 0) dw[(int64_t)t * K + k] = part;
+  }
+}
+
+// dx[t] = sum_k dx_rows[slot[t,k]] + sum_s dx_rows[R + s*T + t]; one rounding.
+template <typename S>
+__global__ __launch_bounds__(kRowBlock) void dispatch_bwd_kernel(const S* __restrict__ dx_rows,
+                                                                 const int32_t* __restrict__ slot,
+                                                                 S* __restrict__ dx, int T, int H,
+                                                                 int K, int Ns) {
+  constexpr int P = Elem<S>::kPerVec;
+  const int t = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (t >= T) return;
+  const int my_slot = lane < K ? slot[(int64_t)t * K + lane] : 0;
+  const int64_t R = (int64_t)T * K;
+  const int nvec = H / P;
+  for (int v = lane; v < nvec; v += kWave) {
+    float acc[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) acc[j] = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int s = __shfl(my_slot, k, kWave);
+      float f[P];
+      Elem<S>::unpack(ld16(reinterpret_cast<const char*>(dx_rows + (int64_t)s * H) + (int64_t)v * 16), f);
+#pragma unroll
+      for (int j = 0; j < P; ++j) acc[j] += f[j];
+    }
+    for (int sh = 0; sh < Ns; ++sh) {
+      float f[P];
+      Elem<S>::unpack(ld16(reinterpret_cast<const char*>(dx_rows + (R + (int64_t)sh * T + t) * H) +
+                           (int64_t)v * 16), f);
+#pragma unroll
+      for (int j = 0; j < P; ++j) acc[j] += f[j];
+    }
+    st16(reinterpret_cast<char*>(dx + (int64_t)t * H) + (int64_t)v * 16, Elem<S>::pack(acc));
+  }
+}
+
+// dl[t, e_k] = w_k (dw_k - sum_j w_j dw_j), zero for unselected experts.
+// One wave per token; lane e writes dl[t, e] for e = lane, lane+64, ...
+__global__ __launch_bounds__(kRowBlock) void route_bwd_kernel(const float* __restrict__ dw,
+                                                              const float* __restrict__ w,
+                                                              const int32_t* __restrict__ idx,
+                                                              float* __restrict__ dl, int T, int E,
+                                                              int K) {
+  const int t = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (t >= T) return;
+  const float my_w = lane < K ? w[(int64_t)t * K + lane] : 0.f;
+  const float my_g = lane < K ? dw[(int64_t)t * K + lane] : 0.f;
+  const int my_e = lane < K ? idx[(int64_t)t * K + lane] : -1;
+  const float inner = wave_sum(my_w * my_g);
+  const float val = my_w * (my_g - inner);
+  for (int e0 = 0; e0 < E; e0 += kWave) {
+    const int e = e0 + lane;
+    float out = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int ek = __shfl(my_e, k, kWave);
+      const float vk = __shfl(val, k, kWave);
+      if (ek == e) out = vk;
+    }
+    if (e < E) dl[(int64_t)t * E + e] = out;
+  }
+}
+
+static inline dim3 row_grid(int T) { return dim3((T + kRowsPerBlock - 1) / kRowsPerBlock); }
+
+hipError_t launch_dispatch(bool is_bf16, const void* x, const int32_t* slot, void* x_perm, int T,
+                           int H, int K, hipStream_t st) {
+  if (is_bf16)
+    dispatch_kernel<uint16_t><<<row_grid(T), kRowBlock, 0, st>>>(
+        static_cast<const uint16_t*>(x), slot, static_cast<uint16_t*>(x_perm), T, H, K);
+  else
+    dispatch_kernel<float><<<row_grid(T), kRowBlock, 0, st>>>(
+        static_cast<const float*>(x), slot, static_cast<float*>(x_perm), T, H, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(bool is_bf16, const void* y, const int32_t* slot, const float* w,
+                          void* out, int T, int H, int K, int Ns, hipStream_t st) {
+  if (is_bf16)
+    combine_kernel<uint16_t><<<row_grid(T), kRowBlock, 0, st>>>(
+        static_cast<const uint16_t*>(y), slot, w, static_cast<uint16_t*>(out), T, H, K, Ns);
+  else
+    combine_kernel<float><<<row_grid(T), kRowBlock, 0, st>>>(
+        static_cast<const float*>(y), slot, w, static_cast<float*>(out), T, H, K, Ns);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(bool is_bf16, const void* dout, const void* y, const int32_t* slot,
+                              const float* w, void* dy, float* dw, int T, int H, int K,
+                              hipStream_t st) {
+  if (is_bf16)
+    combine_bwd_kernel<uint16_t><<<row_grid(T), kRowBlock, 0, st>>>(
+        static_cast<const uint16_t*>(dout), static_cast<const uint16_t*>(y), slot, w,
+        static_cast<uint16_t*>(dy), dw, T, H, K);
+  else
+    combine_bwd_kernel<float><<<row_grid(T), kRowBlock, 0, st>>>(
+        static_cast<const float*>(dout), static_cast<const float*>(y), slot, w,
+        static_cast<float*>(dy), dw, T, H, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_bwd(bool is_bf16, const void* dx_rows, const int32_t* slot, void* dx,
+                               int T, int H, int K, int Ns, hipStream_t st) {
+  if (is_bf16)
+    dispatch_bwd_kernel<uint16_t><<<row_grid(T), kRowBlock, 0, st>>>(
+        static_cast<const uint16_t*>(dx_rows), slot, static_cast<uint16_t*>(dx), T, H, K, Ns);
+  else
+    dispatch_bwd_kernel<float><<<row_grid(T), kRowBlock, 0, st>>>(
+        static_cast<const float*>(dx_rows), slot, static_cast<float*>(dx), T, H, K, Ns);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_bwd(const float* dw, const float* w, const int32_t* idx, float* dl, int T,
+                            int E, int K, hipStream_t st) {
+  route_bwd_kernel<<<row_grid(T), kRowBlock, 0, st>>>(dw, w, idx, dl, T, E, K);
+  return hipGetLastError();
+}
+
+}  // namespace moe

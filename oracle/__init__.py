@@ -8,4 +8,4 @@ from .moe_oracle import (widen, store, route_select, route_weights, route, slot_
                          slot_map_ranks, dispatch, swiglu_up, down_proj, expert_ffn, combine,
                          forward, combine_bwd, swiglu_bwd, input_grad, expert_ffn_bwd_data,
                          expert_ffn_bwd_weight, dispatch_bwd, route_bwd, backward,
-                         token_forward, token_backward, expert_wgrad_columns)
+                         tokens_forward, tokens_backward, expert_wgrad_columns)

@@ -439,47 +439,95 @@ def backward(inp: dict, fwd: dict, dtype: str) -> dict:
 # ---------------------------------------------------------------------------
 
 
-def token_forward(x_row, experts, weights, inp, dtype):
-    """out for one token straight from the definition, no permutation.
-
-    Returns (out_row stored, y rows [K, H] stored)."""
-    acc = np.zeros(x_row.shape[-1], dtype=np.float64)
-    ys = []
-    for e, w in zip(experts, weights):
-        _, _, h = swiglu_up(x_row[None], inp["w1"][e], inp["w3"][e], dtype)
-        y = down_proj(h, inp["w2"][e], dtype)[0]
-        ys.append(y)
-        acc += np.float64(w) * widen(y, dtype)
-    if "ws1" in inp:
-        for s in range(inp["ws1"].shape[0]):
-            _, _, h = swiglu_up(x_row[None], inp["ws1"][s], inp["ws3"][s], dtype)
-            acc += widen(down_proj(h, inp["ws2"][s], dtype)[0], dtype)
-    return store(acc, dtype), np.stack(ys)
+def _expert_weights(inp, e, dtype):
+    """float64 copies of expert e's weights (e >= E: shared expert e - E)."""
+    E = inp["w1"].shape[0]
+    if e < E:
+        return widen(inp["w1"][e], dtype), widen(inp["w3"][e], dtype), widen(inp["w2"][e], dtype)
+    s = e - E
+    return widen(inp["ws1"][s], dtype), widen(inp["ws3"][s], dtype), widen(inp["ws2"][s], dtype)
 
 
-def token_backward(x_row, dout_row, experts, weights, inp, dtype):
-    """dx and dtopk_w of one token straight from the definition.
+def tokens_forward(X, experts, weights, inp, dtype):
+    """out for a few tokens straight from the definition, no permutation.
 
-    Returns (dx_row stored, dw [K] float32)."""
-    g = widen(dout_row, dtype)
-    acc = np.zeros(x_row.shape[-1], dtype=np.float64)
-    dw = np.empty(len(experts), dtype=np.float32)
+    X [n, H] storage rows, experts/weights [n, K] (the route of those tokens).
+    Each (token, k) branch is h = silu(x W1_e) * (x W3_e), y = h W2_e with the
+    layer's storage roundings; out = sum_k w_k y_k (k ascending) + shared
+    experts, rounded once.  Returns (out [n, H] stored, y [n, K, H] stored).
+    """
+    n, K = experts.shape
+    H = X.shape[1]
+    E = inp["w1"].shape[0]
+    Ns = inp["ws1"].shape[0] if "ws1" in inp else 0
+    ys = storage_zeros((n, K, H), dtype)
+    ysh = storage_zeros((Ns, n, H), dtype)
+    for e in sorted(set(experts.ravel().tolist())) + [E + s for s in range(Ns)]:
+        W1, W3, W2 = _expert_weights(inp, e, dtype)
+        if e < E:
+            rows, ks = np.nonzero(experts == e)
+        else:
+            rows = np.arange(n)
+        Xf = widen(X[rows], dtype)
+        a, b = Xf @ W1, Xf @ W3
+        y = store(widen(store(_silu(a) * b, dtype), dtype) @ W2, dtype)
+        if e < E:
+            ys[rows, ks] = y
+        else:
+            ysh[e - E] = y
+    acc = np.zeros((n, H), dtype=np.float64)
+    for k in range(K):
+        acc += weights[:, k].astype(np.float64)[:, None] * widen(ys[:, k], dtype)
+    for s in range(Ns):
+        acc += widen(ysh[s], dtype)
+    return store(acc, dtype), ys
 
-    def branch(W1, W3, W2, dy_row):
-        a, b, h = swiglu_up(x_row[None], W1, W3, dtype)
-        y = down_proj(h, W2, dtype)[0]
-        da, db = swiglu_bwd(dy_row[None], W2, a, b, dtype)
-        return y, widen(input_grad(da, db, W1, W3, dtype)[0], dtype)
 
-    for k, (e, w) in enumerate(zip(experts, weights)):
-        dy = store(np.float64(w) * g, dtype)
-        y, dxk = branch(inp["w1"][e], inp["w3"][e], inp["w2"][e], dy)
-        dw[k] = np.float32(np.dot(g, widen(y, dtype)))
-        acc += dxk
-    if "ws1" in inp:
-        for s in range(inp["ws1"].shape[0]):
-            _, dxs = branch(inp["ws1"][s], inp["ws3"][s], inp["ws2"][s], dout_row)
-            acc += dxs
+def tokens_backward(X, G, experts, weights, inp, dtype):
+    """dx and dtopk_w for a few tokens straight from the definition.
+
+    X, G [n, H] storage rows of x and dout.  Per branch: dy = w_k dout
+    (stored), dh = dy W2_e^T, da/db from the branch's saved a, b, dx_k =
+    da W1_e^T + db W3_e^T (stored); dx = sum_k dx_k (k ascending) + shared
+    branches (dy = dout), rounded once; dw_k = <dout, y_k>.
+    Returns (dx [n, H] stored, dw [n, K] float32).
+    """
+    n, K = experts.shape
+    H = X.shape[1]
+    E = inp["w1"].shape[0]
+    Ns = inp["ws1"].shape[0] if "ws1" in inp else 0
+    Gf = widen(G, dtype)
+    dxk = np.zeros((n, K, H), dtype=np.float64)
+    dxs = np.zeros((Ns, n, H), dtype=np.float64)
+    dw = np.zeros((n, K), dtype=np.float32)
+    for e in sorted(set(experts.ravel().tolist())) + [E + s for s in range(Ns)]:
+        W1, W3, W2 = _expert_weights(inp, e, dtype)
+        if e < E:
+            rows, ks = np.nonzero(experts == e)
+            dy = store(weights[rows, ks].astype(np.float64)[:, None] * Gf[rows], dtype)
+        else:
+            rows = np.arange(n)
+            dy = G
+        Xf = widen(X[rows], dtype)
+        af, bf = Xf @ W1, Xf @ W3
+        a, b = store(af, dtype), store(bf, dtype)
+        y = store(widen(store(_silu(af) * bf, dtype), dtype) @ W2, dtype)
+        dh = widen(dy, dtype) @ W2.T
+        A, B = widen(a, dtype), widen(b, dtype)
+        sg = _sigmoid(A)
+        da = store(dh * B * sg * (1.0 + A * (1.0 - sg)), dtype)
+        db = store(dh * A * sg, dtype)
+        dx = widen(store(widen(da, dtype) @ W1.T + widen(db, dtype) @ W3.T, dtype), dtype)
+        if e < E:
+            dxk[rows, ks] = dx
+            dw[rows, ks] = np.einsum("nh,nh->n", Gf[rows], widen(y, dtype)).astype(np.float32)
+        else:
+            dxs[e - E] = dx
+    acc = np.zeros((n, H), dtype=np.float64)
+    for k in range(K):
+        acc += dxk[:, k]
+    for s in range(Ns):
+        acc += dxs[s]
     return store(acc, dtype), dw
 
 

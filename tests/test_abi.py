@@ -1,0 +1,88 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point include/moe.h declares, and rejects bad arguments with the
+documented status codes before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_moe_route_histogram_amd as M
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(M.lib_path()):
+        pytest.fail("libmoe.so is not built (run __graft_entry__.build())")
+    return M.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(lib, n), n
+    # the binding wraps every declared entry point under the same name
+    for n in names:
+        assert callable(getattr(M, n)), n
+
+
+def test_status_strings(lib):
+    assert M.moe_status_str(0) == "MOE_OK"
+    assert M.moe_status_str(3) == "MOE_EWORKSPACE"
+    assert M.moe_status_str(99) == "MOE_UNKNOWN"
+
+
+def _dims(**kw):
+    base = dict(T=64, H=128, E=8, K=2, I=256, n_shared=0, dtype=M.BF16)
+    base.update(kw)
+    return M.Dims(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), 1), (dict(E=0), 2), (dict(E=257), 2), (dict(K=0), 2), (dict(K=9), 2),
+    (dict(E=128, K=65), 2), (dict(H=100), 2), (dict(I=96), 2), (dict(n_shared=9), 2),
+    (dict(dtype=5), 2),
+])
+def test_bad_dims_rejected_without_launch(lib, kw, status):
+    d = _dims(**kw)
+    assert lib.moe_workspace_bytes(ctypes.byref(d)) == 0
+    st = lib.moe_route(ctypes.byref(d), *([ctypes.c_void_p(16)] * 7), ctypes.c_void_p(256), 1 << 20, None)
+    assert st == status
+    assert M.moe_last_error() != ""
+
+
+def test_null_misaligned_and_workspace_errors(lib):
+    d = _dims()
+    need = lib.moe_workspace_bytes(ctypes.byref(d))
+    assert need > 0 and need % 256 == 0
+    p = ctypes.c_void_p(4096)
+    # null pointer
+    st = lib.moe_route(ctypes.byref(d), None, p, p, p, p, p, p, p, need, None)
+    assert st == 1 and "logits" in M.moe_last_error()
+    # misaligned pointer
+    st = lib.moe_dispatch(ctypes.byref(d), ctypes.c_void_p(4098), p, p, None)
+    assert st == 1 and "aligned" in M.moe_last_error()
+    # workspace too small / missing
+    st = lib.moe_route(ctypes.byref(d), p, p, p, p, p, p, p, p, need - 1, None)
+    assert st == 3
+    st = lib.moe_route(ctypes.byref(d), p, p, p, p, p, p, p, None, need, None)
+    assert st == 3
+    # shared experts require their weights
+    d2 = _dims(n_shared=2)
+    st = lib.moe_expert_ffn_up(ctypes.byref(d2), p, p, p, p, p, None, p, p, p, p, 1 << 30, None)
+    assert st == 1
+
+
+def test_workspace_grows_with_tokens(lib):
+    a = lib.moe_workspace_bytes(ctypes.byref(_dims(T=64)))
+    b = lib.moe_workspace_bytes(ctypes.byref(_dims(T=131072)))
+    assert b > a
