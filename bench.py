@@ -1,0 +1,225 @@
+"""Throughput of the MoE expert layer (forward + backward) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
+                    [--unfused] [--no-cpu-baseline] [--cpu-tokens N]
+
+One step = one pass of the whole layer over one batch of synthetic, seeded
+inputs already resident in HBM: route (top-k, histogram, slot map) ->
+dispatch -> grouped SwiGLU GEMM -> down GEMM -> combine, then combine backward
+-> FFN input gradients -> FFN weight gradients -> dispatch backward -> gate
+backward.  Prints one JSON line.  Default workload: the Mixtral-like layer
+(T=4096 tokens, H=4096, E=8, top-2, I=14336, bf16).
+
+Each library call inside the timed steps is bracketed by HIP events recorded
+on the stream the call launches on, so per-call device times are measured on
+the very steps that are timed.  The roofline entry is computed for the call
+with the largest total time from its algorithmic flop (or byte) count.
+The CPU baseline times the oracle (plain fp64 numpy) on a bounded sample of
+the same layer: the first --cpu-tokens tokens, full expert weights.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd+bwd tokens/sec on 1 MI355X; % MFMA peak (GEMM), % HBM BW"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--unfused", action="store_true", help="time the unfused forward calls")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=128)
+    ap.add_argument("--fwd-only", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic_work(d, b):
+    """Algorithmic flop / byte counts per call (b = bytes per element)."""
+    T, H, E, K, I, Ns, R = d.T, d.H, d.E, d.K, d.I, d.n_shared, d.R
+    RA = R + Ns * T
+    gemm = lambda rows, m: 2.0 * rows * H * I * m
+    return {
+        "route": ("hbm", 4.0 * T * E + 8.0 * T * K + 4.0 * E + 8.0 * R),
+        "dispatch": ("hbm", b * T * H + b * R * H + 4.0 * R),
+        "ffn_up": ("mfma", gemm(RA, 2)),
+        "ffn_down": ("mfma", gemm(RA, 1)),
+        "dispatch_ffn": ("mfma", gemm(RA, 2)),
+        "ffn_combine": ("mfma", gemm(RA, 1)),
+        "combine": ("hbm", b * R * H + b * Ns * T * H + b * T * H + 8.0 * R),
+        "combine_bwd": ("hbm", b * T * H + 2 * b * R * H + 12.0 * R),
+        "ffn_bwd_data": ("mfma", gemm(RA, 3)),
+        "ffn_bwd_weight": ("mfma", gemm(RA, 3)),
+        "dispatch_bwd": ("hbm", b * RA * H + b * T * H + 4.0 * R),
+        "route_bwd": ("hbm", 12.0 * T * K + 4.0 * T * E),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the layer would shard by expert across GPUs, which is not built here)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import combine_moe_route_histogram_amd as M
+    from combine_moe_route_histogram_amd import layer as L
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = synth.config(args.workload)
+    backward = ("bwd" in cfg.passes) and not args.fwd_only
+    t_gen = time.time()
+    inp = synth.make_inputs(cfg, with_grad=backward)
+    p = {k: synth.to_torch(v, "cuda") for k, v in inp.items()}
+    gen_s = time.time() - t_gen
+    d = L.make_dims(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.n_shared, cfg.dtype)
+    b = L.Buffers(d, backward=backward)
+    stream = torch.cuda.current_stream()
+    fused = not args.unfused
+
+    calls = []  # (name, start_event, end_event)
+
+    def timed(name, fn, *a):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn(*a)
+        e1.record(stream)
+        calls.append((name, e0, e1))
+
+    def step():
+        timed("route", L.route, b, p)
+        if fused:
+            timed("dispatch_ffn", M.moe_dispatch_ffn, d, p["x"], b.slot_src, b.offsets, p["w1"],
+                  p["w3"], p.get("ws1"), p.get("ws3"), b.x_perm, b.ab, b.h, b.ws)
+            timed("ffn_combine", M.moe_ffn_combine, d, b.h, b.offsets, p["w2"], p.get("ws2"),
+                  b.slot, b.topk_w, b.y, b.out, b.ws)
+        else:
+            timed("dispatch", M.moe_dispatch, d, p["x"], b.slot, b.x_perm)
+            timed("ffn_up", M.moe_expert_ffn_up, d, b.x_perm, p["x"], b.offsets, p["w1"], p["w3"],
+                  p.get("ws1"), p.get("ws3"), b.ab, b.h, b.ws)
+            timed("ffn_down", M.moe_expert_ffn_down, d, b.h, b.offsets, p["w2"], p.get("ws2"),
+                  b.y, b.ws)
+            timed("combine", M.moe_combine, d, b.y, b.slot, b.topk_w, b.out)
+        if backward:
+            timed("combine_bwd", M.moe_combine_bwd, d, p["dout"], b.y, b.slot, b.topk_w, b.dy,
+                  b.dtopk_w)
+            timed("ffn_bwd_data", M.moe_expert_ffn_bwd_data, d, b.dy, p.get("dout"), b.offsets,
+                  p["w1"], p["w3"], p["w2"], p.get("ws1"), p.get("ws3"), p.get("ws2"), b.ab,
+                  b.dab, b.dx_rows, b.ws)
+            timed("ffn_bwd_weight", M.moe_expert_ffn_bwd_weight, d, b.x_perm, p["x"], b.h, b.dy,
+                  p.get("dout"), b.dab, b.offsets, b.dw1, b.dw3, b.dw2, b.dws1, b.dws3, b.dws2,
+                  b.ws)
+            timed("dispatch_bwd", M.moe_dispatch_bwd, d, b.dx_rows, b.slot, b.dx)
+            timed("route_bwd", M.moe_route_bwd, d, b.dtopk_w, b.topk_w, b.topk_idx, b.dlogits)
+
+    # a fused entry point that is not available falls back to nothing: fail loudly
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    calls.clear()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = cfg.T / (wall / args.steps)
+
+    per_call = {}
+    for name, e0, e1 in calls:
+        per_call.setdefault(name, []).append(e0.elapsed_time(e1))
+    per_call_ms = {k: float(np.mean(v)) for k, v in per_call.items()}
+    bpe = 2 if cfg.dtype == "bf16" else 4
+    work = algorithmic_work(d, bpe)
+    breakdown = {}
+    for k, ms in per_call_ms.items():
+        kind, amount = work[k]
+        if kind == "mfma":
+            rate = amount / (ms * 1e-3) / 1e12
+            peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+            breakdown[k] = {"ms": round(ms, 4), "TFLOP/s": round(rate, 1), "frac": round(rate / peak, 4)}
+        else:
+            rate = amount / (ms * 1e-3) / 1e9
+            breakdown[k] = {"ms": round(ms, 4), "GB/s": round(rate, 1), "frac": round(rate / PEAK_HBM_GBS, 4)}
+    dom = max(per_call_ms, key=per_call_ms.get)
+    kind, amount = work[dom]
+    if kind == "mfma":
+        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+        ach = amount / (per_call_ms[dom] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                    "work_per_launch": amount}
+    else:
+        ach = amount / (per_call_ms[dom] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                    "work_per_launch": amount}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, inp, args.cpu_tokens, backward)
+
+    line = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} E={cfg.E} top-{cfg.K} I={cfg.I}"
+                               f" shared={cfg.n_shared} {cfg.dtype} {'fwd+bwd' if backward else 'fwd'}",
+                   "T": cfg.T, "H": cfg.H, "E": cfg.E, "K": cfg.K, "I": cfg.I,
+                   "n_shared": cfg.n_shared, "passes": "fwd+bwd" if backward else "fwd",
+                   "path": "fused" if fused else "unfused"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_call": breakdown,
+        "input_gen_s": round(gen_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, inp, n_tokens, backward):
+    """The oracle as it stands, on the first n_tokens tokens with full weights."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    n = min(n_tokens, cfg.T)
+    sub = dict(inp)
+    for k in ("logits", "x", "dout"):
+        if k in sub:
+            sub[k] = np.ascontiguousarray(inp[k][:n])
+    t0 = time.perf_counter()
+    f = O.forward(sub, cfg.K, cfg.dtype)
+    if backward:
+        O.backward(sub, f, cfg.dtype)
+    sec = time.perf_counter() - t0
+    return {"value": round(n / sec, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {cfg.T} tokens, full expert weights, "
+                      f"{'fwd+bwd' if backward else 'fwd'}, fp64 numpy; {sec:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -60,15 +60,31 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return (bid % 8) * (nblocks / 8) + bid / 8;
 }
 
+// Logical tile -> (row tile, column tile).  Row tiles are taken in bands of
+// kBandM; inside a band the column tiles advance slowest, so the tiles an XCD
+// runs at the same time form a kBandM x (concurrent / kBandM) block: each
+// operand slice they load is shared by several of them through L2.
+constexpr int kBandM = 8;
+__device__ __forceinline__ void band_order(int L, int mt_count, int nt_count, int& tm, int& tn) {
+  const int band_tiles = kBandM * nt_count;
+  const int band = L / band_tiles;
+  const int rem = L - band * band_tiles;
+  const int rows = min(kBandM, mt_count - band * kBandM);
+  tn = rem / rows;
+  tm = band * kBandM + (rem - tn * rows);
+}
+
 template <class C>
 __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(GemmArgs g, int mt_count, int nt_count) {
-  extern __shared__ __align__(16) uint16_t smem_bf[];
+  __shared__ __align__(16) uint8_t st0[C::STAGE_BYTES];
+  __shared__ __align__(16) uint8_t st1[C::STAGE_BYTES];
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   if (L >= mt_count * nt_count) return;
-  const int tm = L % mt_count, tn = L / mt_count;
+  int tm, tn;
+  band_order(L, mt_count, nt_count, tm, tn);
   const TileDesc<uint16_t> d = decode_tile<uint16_t, C::KIND, C::BM, C::BN>(g, tm, tn);
   if (d.skip) return;
-  run_tile_bf16<C>(g, d, smem_bf);
+  run_tile_bf16<C>(g, d, st0, st1);
 }
 
 template <int KIND>
@@ -82,22 +98,32 @@ __global__ __launch_bounds__(kF32NT) void gemm_f32_kernel(GemmArgs g, int mt_cou
   run_tile_f32<KIND>(g, d, smem_f);
 }
 
-// bf16 tile configurations per kind.
+// bf16 tile configurations per kind: BM, BN, waves along M, waves along N.
+#ifndef MOE_CFG_UP
+#define MOE_CFG_UP 128, 256, 2, 2, 2
+#endif
+#ifndef MOE_CFG_DOWN
+#define MOE_CFG_DOWN 128, 256, 2, 2, 2
+#endif
+#ifndef MOE_CFG_BWD_UP
+#define MOE_CFG_BWD_UP 128, 256, 2, 2, 2
+#endif
+#ifndef MOE_CFG_BWD_DOWN
+#define MOE_CFG_BWD_DOWN 128, 256, 2, 2, 2
+#endif
+#ifndef MOE_CFG_WG_UP
+#define MOE_CFG_WG_UP 128, 256, 2, 2, 2
+#endif
+#ifndef MOE_CFG_WG_DOWN
+#define MOE_CFG_WG_DOWN 128, 256, 2, 2, 2
+#endif
 template <int KIND> struct BfPick;
-template <> struct BfPick<kUp> { using C = BfCfg<kUp, 128, 128, 2, 2>; };
-template <> struct BfPick<kDown> { using C = BfCfg<kDown, 128, 128, 2, 2>; };
-template <> struct BfPick<kBwdUp> { using C = BfCfg<kBwdUp, 128, 128, 2, 2>; };
-template <> struct BfPick<kBwdDown> { using C = BfCfg<kBwdDown, 128, 128, 2, 2>; };
-template <> struct BfPick<kWgUp> { using C = BfCfg<kWgUp, 128, 128, 2, 2>; };
-template <> struct BfPick<kWgDown> { using C = BfCfg<kWgDown, 128, 128, 2, 2>; };
-
-template <class C>
-static hipError_t set_lds_limit() {
-  static hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<C>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               C::LDS_BYTES);
-  return once;
-}
+template <> struct BfPick<kUp> { using C = BfCfg<kUp, MOE_CFG_UP>; };
+template <> struct BfPick<kDown> { using C = BfCfg<kDown, MOE_CFG_DOWN>; };
+template <> struct BfPick<kBwdUp> { using C = BfCfg<kBwdUp, MOE_CFG_BWD_UP>; };
+template <> struct BfPick<kBwdDown> { using C = BfCfg<kBwdDown, MOE_CFG_BWD_DOWN>; };
+template <> struct BfPick<kWgUp> { using C = BfCfg<kWgUp, MOE_CFG_WG_UP>; };
+template <> struct BfPick<kWgDown> { using C = BfCfg<kWgDown, MOE_CFG_WG_DOWN>; };
 
 template <int KIND>
 static hipError_t launch_kind(bool is_bf16, GemmArgs a, int4* mtiles_ws, int32_t* n_ws,
@@ -120,10 +146,8 @@ static hipError_t launch_kind(bool is_bf16, GemmArgs a, int4* mtiles_ws, int32_t
   if (tiles <= 0) return hipSuccess;
   if (tiles > INT_MAX - 8) return hipErrorInvalidValue;
   if (is_bf16) {
-    hipError_t e = set_lds_limit<C>();
-    if (e != hipSuccess) return e;
     const int grid = (int)((tiles + 7) / 8 * 8);
-    gemm_bf16_kernel<C><<<grid, C::NT, C::LDS_BYTES, st>>>(a, mt_count, nt_count);
+    gemm_bf16_kernel<C><<<grid, C::NT, 0, st>>>(a, mt_count, nt_count);
   } else {
     gemm_f32_kernel<KIND><<<(int)tiles, kF32NT, 0, st>>>(a, mt_count, nt_count);
   }

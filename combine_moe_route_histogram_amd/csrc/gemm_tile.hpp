@@ -227,144 +227,189 @@ __device__ __forceinline__ void emit(const GemmArgs& g, const TileDesc<S>& d, in
 }
 
 // ----------------------------------------------------------------- bf16 ----
+//
+// LDS layouts (one stage; a stage holds one 64-deep k slice of both operands):
+//  K-contiguous operand ("KC"): rows = m (or n), 64 k per row = 128 bytes;
+//    16-byte chunk c of row r is stored at chunk c ^ ((r >> 1) & 7).  A wave's
+//    16-byte fragment reads of 16 consecutive rows then hit 16 distinct bank
+//    groups.
+//  MN-contiguous operand ("MN"): rows = k (64 of them), the m (or n) columns
+//    contiguous, in one or two sub-tiles of >= 128 columns (paired kinds keep
+//    their two source tensors in separate sub-tiles); 16-byte chunk c of row k
+//    is stored at chunk c ^ (4 * (k % 4)), which keeps the transposed reads
+//    below free of bank conflicts.
+// Operands move global -> LDS with buffer loads that write LDS directly (lane
+// l of an instruction fills bytes [16 l, 16 l + 16) of a 1 KiB LDS block), so
+// no register staging or VALU work is spent on the copy.  Rows or k outside
+// the valid range use an out-of-range buffer offset and land as zeros.
+// Fragment reads: KC operands with ds_read_b128 (8 consecutive k of one row);
+// MN operands with two ds_read_b64_tr_b16 (gfx950 LDS transpose read: in each
+// 16-lane group, lanes 4j..4j+3 point at 16 consecutive columns of k row j and
+// lane i receives column i of the 4 rows), giving the same 8 consecutive k.
 
-// LDS element offset of (row, k): rows of kBK bf16, 16-byte chunks swizzled.
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 3);
+typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4* lds_i16x4_t;
+
+constexpr uint32_t kBufRecords = 0x7FFFFFF0u;
+constexpr uint32_t kBufInvalid = 0x80000000u;
+constexpr int kBufDword3 = 0x00020000;  // raw buffer, 32-bit data (gfx9 family)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, kBufRecords, kBufDword3);
 }
 
-// K-contiguous operand: BMN rows x 64 k, 16-byte chunks.
-template <int BMN, int NT>
-struct LoadKC {
-  static constexpr int kN = BMN * (kBK / 8) / NT;
-  static_assert(kN >= 1 && BMN * (kBK / 8) % NT == 0, "tile/threads mismatch");
-  u32x4 r[kN];
-  // p points at element (mn = 0, k = k0) of the tile's rows; s_mn = row stride.
-  __device__ __forceinline__ void load(const uint16_t* p, int64_t s_mn, int mn_valid, int tid) {
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds_block, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t)lds_block, 16, voff, 0, 0, 0);
+}
+
+// Byte offset of (row, 16-byte chunk) inside a KC stage tile.
+__device__ __forceinline__ uint32_t kc_off(int row, int chunk) {
+  return (uint32_t)(row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4));
+}
+// Byte offset of (k, column) inside an MN sub-tile of `cols` columns.
+__device__ __forceinline__ uint32_t mn_off(int k, int col, int cols) {
+  return (uint32_t)(k * cols * 2 + ((((col >> 3) ^ (4 * (k & 3)))) << 4) + (col & 7) * 2);
+}
+
+// Global -> LDS copy of one operand stage.
+//  KC: rows BMN, 8 rows per 1 KiB instruction.
+//  MN: NH sub-tiles of HMN columns, 64 k rows, 1024 / (2 HMN) rows per instruction.
+template <int BMN, int NW, bool MN, int NH>
+struct DmaOperand {
+  static constexpr int kHMN = BMN / NH;
+  static constexpr int kInstr = BMN * kBK * 2 / 1024;      // 1 KiB instructions per stage
+  static constexpr int kPerWave = kInstr / NW;
+  static_assert(kInstr % NW == 0, "stage copy must split evenly over the waves");
+  static_assert(!MN || kHMN >= 128, "MN sub-tiles need >= 128 columns");
+  static_assert(MN || NH == 1, "KC operands have one source");
+  uint32_t off[kPerWave];   // per-lane byte offset (relative to the k slice start) or invalid
+  int krow[kPerWave];       // MN: k row of this lane (for the ragged-k check)
+  // s = row stride (KC) or k stride (MN) in elements; mn_valid per sub-tile.
+  __device__ __forceinline__ void init(int64_t s, int mn_valid, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < kN; ++i) {
-      const int id = tid + i * NT;
-      const int mn = id >> 3, ch = id & 7;
-      if (mn < mn_valid)
-        r[i] = ld16(p + (int64_t)mn * s_mn + ch * 8);
-      else
-        r[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < kPerWave; ++i) {
+      const int q = wave + NW * i;                           // instruction index in the stage
+      if constexpr (!MN) {
+        const int r = 8 * q + (lane >> 3);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        off[i] = r < mn_valid ? (uint32_t)(r * s * 2 + c * 16) : kBufInvalid;
+        krow[i] = 0;
+      } else {
+        constexpr int kQHalf = kHMN * kBK * 2 / 1024;        // instructions per sub-tile
+        const int qh = q % kQHalf;
+        const int byte = qh * 1024 + 16 * lane;
+        const int k = byte / (2 * kHMN);
+        const int p = (byte % (2 * kHMN)) / 16;
+        const int col = (p ^ (4 * (k & 3))) * 8;
+        off[i] = col < mn_valid ? (uint32_t)(k * s * 2 + col * 2) : kBufInvalid;
+        krow[i] = k;
+      }
     }
   }
-  __device__ __forceinline__ void store(uint16_t* s, int tid) const {
+  // Issue the copy of one k slice.  src0/src1: operand at (k slice start,
+  // column 0) of sub-tile 0/1 (KC: row 0 at k0); k_valid: valid k rows (MN).
+  __device__ __forceinline__ void issue(uint8_t* stage, const uint16_t* src0, const uint16_t* src1,
+                                        int k_valid, int wave) const {
 #pragma unroll
-    for (int i = 0; i < kN; ++i) {
-      const int id = tid + i * NT;
-      st16(s + lds_off(id >> 3, id & 7), r[i]);
+    for (int i = 0; i < kPerWave; ++i) {
+      const int q = wave + NW * i;
+      const uint16_t* src = src0;
+      if constexpr (NH == 2) {
+        constexpr int kQHalf = kHMN * kBK * 2 / 1024;
+        if (q >= kQHalf) src = src1;
+      }
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(src);
+      uint32_t o = off[i];
+      if constexpr (MN) o = krow[i] < k_valid ? o : kBufInvalid;
+      dma16(rs, stage + q * 1024, o);
     }
   }
 };
 
-// MN-contiguous operand: 64 k rows x BMN columns, read as 8(k) x 4(mn)
-// blocks of 8-byte loads, transposed in registers, stored K-contiguous.
-template <int BMN, int NT, bool PAIRED>
-struct LoadMN {
-  static constexpr int kBlocksMN = BMN / 4;
-  static constexpr int kNB = (kBK / 8) * kBlocksMN / NT;
-  static_assert(kNB >= 1 && (kBK / 8) * kBlocksMN % NT == 0, "tile/threads mismatch");
-  u32x2 r[kNB][8];
-  // p0 (and p1 for paired) point at element (k = k0, mn = 0); s_k = k stride.
-  // mn_valid counts per half when PAIRED; k_valid = valid k rows from k0.
-  __device__ __forceinline__ void load(const uint16_t* p0, const uint16_t* p1, int64_t s_k,
-                                       int mn_valid, int k_valid, int tid) {
-#pragma unroll
-    for (int b = 0; b < kNB; ++b) {
-      const int id = tid + b * NT;
-      const int kb = id / kBlocksMN, mb = id - kb * kBlocksMN;
-      int mn = mb * 4;
-      const uint16_t* p = p0;
-      if constexpr (PAIRED) {
-        if (mn >= BMN / 2) {
-          p = p1;
-          mn -= BMN / 2;
-        }
-      }
-      const bool mn_ok = mn < mn_valid;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int k = kb * 8 + j;
-        if (mn_ok && k < k_valid)
-          r[b][j] = *reinterpret_cast<const u32x2*>(p + (int64_t)k * s_k + mn);
-        else
-          r[b][j] = u32x2{0u, 0u};
-      }
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* s, int tid) const {
-#pragma unroll
-    for (int b = 0; b < kNB; ++b) {
-      const int id = tid + b * NT;
-      const int kb = id / kBlocksMN, mb = id - kb * kBlocksMN;
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
-        u32x4 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          o[q] = __builtin_amdgcn_perm(r[b][2 * q + 1][n >> 1], r[b][2 * q][n >> 1], sel);
-        st16(s + lds_off(mb * 4 + n, kb), o);
-      }
-    }
-  }
-};
-
-template <int KIND_, int BM_, int BN_, int WGM_, int WGN_>
+template <int KIND_, int BM_, int BN_, int WGM_, int WGN_, int STAGES_>
 struct BfCfg {
-  static constexpr int KIND = KIND_, BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
-  static constexpr int NT = WGM * WGN * kWave;
+  static constexpr int KIND = KIND_, BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, STAGES = STAGES_;
+  static constexpr int NW = WGM * WGN, NT = NW * kWave;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int MI = WM / 32, NJ = WN / 32;
   static constexpr bool PAIRED = KindTraits<KIND>::kPaired;
-  static constexpr int LDS_BYTES = 2 * (BM + BN) * kBK * 2;
+  static constexpr bool A_MN = KindTraits<KIND>::kAMn, B_MN = KindTraits<KIND>::kBMn;
+  static constexpr int B_NH = PAIRED ? 2 : 1;
+  static constexpr int A_BYTES = BM * kBK * 2, B_BYTES = BN * kBK * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be made of 32x32 blocks");
   static_assert(!PAIRED || (NJ % 2 == 0), "paired kinds need an even number of N blocks");
+  static_assert(STAGES >= 2, "at least double buffering");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-// B-tile LDS row of the first column of wave wn's N-block j.  Paired kinds
-// keep gate columns in rows [0, BN/2) and up columns in [BN/2, BN); block j and
-// block j + NJ/2 of a wave then cover the same output column.
+// Fragment reads.  kc_frag: 8 consecutive k (16-byte chunk ch) of row `row`.
+__device__ __forceinline__ bf16x8 kc_frag(const uint8_t* tile, int row, int ch) {
+  return *reinterpret_cast<const bf16x8*>(tile + kc_off(row, ch));
+}
+// mn_frag: for MFMA lane l, column col0 + (l % 32) and k rows 8 * (l / 32) +
+// 16 * ks .. + 8 of an MN sub-tile of `cols` columns.
+__device__ __forceinline__ bf16x8 mn_frag(const uint8_t* tile, int cols, int col0, int ks, int lane) {
+  const int h = lane >> 4, i = lane & 15;
+  const int k = 16 * ks + 8 * (h >> 1) + (i >> 2);
+  const int col = col0 + 16 * (h & 1) + 4 * (i & 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t)(tile + mn_off(k, col, cols)));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t)(tile + mn_off(k + 4, col, cols)));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// First column (within its B sub-tile) of wave wn's N-block j, and the sub-tile.
+// Paired kinds: block j and block j + NJ/2 cover the same output column, from
+// the first and the second source tensor.
 template <class C>
-__device__ __forceinline__ int b_row(int wn, int j) {
+__device__ __forceinline__ void b_block(int wn, int j, int& sub, int& col) {
   if constexpr (C::PAIRED) {
     constexpr int HJ = C::NJ / 2;
-    return (j / HJ) * (C::BN / 2) + wn * (C::WN / 2) + 32 * (j % HJ);
+    sub = j / HJ;
+    col = wn * (C::WN / 2) + 32 * (j % HJ);
   } else {
-    return wn * C::WN + 32 * j;
+    sub = 0;
+    col = wn * C::WN + 32 * j;
   }
 }
 
-// The whole tile: K loop over LDS double buffers, then the epilogue.
+// The whole tile: two LDS k slices (separate LDS objects, so the compiler can
+// tell the direct loads into one from the fragment reads of the other) filled
+// alternately, MFMA over each slice with the next k step's fragments in
+// flight, then the epilogue.  The barrier at the top of each slice both waits
+// for that slice's loads and frees the other slice for the next loads, which
+// then run during the whole MFMA pass over this slice.
 template <class C>
-__device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d, uint16_t* smem) {
-  constexpr int BM = C::BM, BN = C::BN, NT = C::NT, MI = C::MI, NJ = C::NJ;
-  using TA = KindTraits<C::KIND>;
+__device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d, uint8_t* st0,
+                              uint8_t* st1) {
+  constexpr int MI = C::MI, NJ = C::NJ;
+  static_assert(C::STAGES == 2, "two LDS slices");
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / C::WGN, wn = wave % C::WGN;
-  uint16_t* sA[2] = {smem, smem + BM * kBK};
-  uint16_t* sB[2] = {smem + 2 * BM * kBK, smem + 2 * BM * kBK + BN * kBK};
 
-  typename std::conditional<TA::kAMn, LoadMN<BM, NT, false>, LoadKC<BM, NT>>::type la;
-  typename std::conditional<TA::kBMn, LoadMN<BN, NT, C::PAIRED>, LoadKC<BN, NT>>::type lb;
+  DmaOperand<C::BM, C::NW, C::A_MN, 1> da;
+  DmaOperand<C::BN, C::NW, C::B_MN, C::B_NH> db;
+  if constexpr (C::A_MN) da.init(d.a_sk, d.m_valid, wave, lane); else da.init(d.a_sm, d.m_valid, wave, lane);
+  if constexpr (C::B_MN) db.init(d.b_sk, d.n_valid, wave, lane); else db.init(d.b_sn, d.n_valid, wave, lane);
 
-  auto load = [&](int kt) {
+  const int nk = (d.k_len + kBK - 1) / kBK;
+  auto issue = [&](uint8_t* st, int kt) {
     const int k0 = kt * kBK;
-    if constexpr (TA::kAMn)
-      la.load(d.a + (int64_t)k0 * d.a_sk, nullptr, d.a_sk, d.m_valid, d.k_len - k0, tid);
+    if constexpr (C::A_MN)
+      da.issue(st, d.a + (int64_t)k0 * d.a_sk, nullptr, d.k_len - k0, wave);
     else
-      la.load(d.a + k0, d.a_sm, d.m_valid, tid);
-    if constexpr (TA::kBMn) {
-      lb.load(d.b0 + (int64_t)k0 * d.b_sk, C::PAIRED ? d.b1 + (int64_t)k0 * d.b_sk : nullptr,
-              d.b_sk, d.n_valid, d.k_len - k0, tid);
-    } else {
-      const uint16_t* p = k0 < d.ksplit ? d.b0 + k0 : d.b1 + (k0 - d.ksplit);
-      lb.load(p, d.b_sn, d.n_valid, tid);
-    }
+      da.issue(st, d.a + k0, nullptr, 0, wave);
+    if constexpr (C::B_MN)
+      db.issue(st + C::A_BYTES, d.b0 + (int64_t)k0 * d.b_sk,
+               C::PAIRED ? d.b1 + (int64_t)k0 * d.b_sk : nullptr, d.k_len - k0, wave);
+    else
+      db.issue(st + C::A_BYTES, k0 < d.ksplit ? d.b0 + k0 : d.b1 + (k0 - d.ksplit), nullptr, 0, wave);
   };
 
   f32x16 acc[MI][NJ];
@@ -375,40 +420,57 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d, ui
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = (d.k_len + kBK - 1) / kBK;
-  if (nk > 0) {
-    load(0);
-    la.store(sA[0], tid);
-    lb.store(sB[0], tid);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load(kt + 1);
-    const uint16_t* a_s = sA[cur];
-    const uint16_t* b_s = sB[cur];
+  int a_row[MI], b_sub[NJ], b_col[NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) a_row[i] = wm * C::WM + 32 * i;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) b_block<C>(wn, j, b_sub[j], b_col[j]);
+  constexpr int kBSubBytes = C::B_BYTES / C::B_NH;
+  constexpr int kBCols = C::BN / C::B_NH;
+
+  auto frags = [&](const uint8_t* st, int ks, bf16x8 (&av)[MI], bf16x8 (&bv)[NJ]) {
+    const uint8_t* ta = st;
+    const uint8_t* tb = st + C::A_BYTES;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      if constexpr (C::A_MN)
+        av[i] = mn_frag(ta, C::BM, a_row[i], ks, lane);
+      else
+        av[i] = kc_frag(ta, a_row[i] + (lane & 31), 2 * ks + (lane >> 5));
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if constexpr (C::B_MN)
+        bv[j] = mn_frag(tb + b_sub[j] * kBSubBytes, kBCols, b_col[j], ks, lane);
+      else
+        bv[j] = kc_frag(tb, b_col[j] + (lane & 31), 2 * ks + (lane >> 5));
+    }
+  };
+  auto compute = [&](const uint8_t* st) {
+    bf16x8 av[2][MI], bv[2][NJ];
+    frags(st, 0, av[0], bv[0]);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int ch = 2 * ks + (lane >> 5);
-      bf16x8 av[MI], bv[NJ];
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-        av[i] = *reinterpret_cast<const bf16x8*>(a_s + lds_off(wm * C::WM + 32 * i + (lane & 31), ch));
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        bv[j] = *reinterpret_cast<const bf16x8*>(b_s + lds_off(b_row<C>(wn, j) + (lane & 31), ch));
+      if (ks + 1 < kBK / 16) frags(st, ks + 1, av[(ks + 1) & 1], bv[(ks + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks & 1][i], bv[ks & 1][j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) {
-      la.store(sA[cur ^ 1], tid);
-      lb.store(sB[cur ^ 1], tid);
-    }
-    __syncthreads();
+  };
+
+  if (nk > 0) issue(st0, 0);
+  for (int kt = 0; kt < nk; kt += 2) {
+    __syncthreads();                       // slice kt (st0) landed; st1 free
+    if (kt + 1 < nk) issue(st1, kt + 1);
+    compute(st0);
+    if (kt + 1 >= nk) break;
+    __syncthreads();                       // slice kt+1 (st1) landed; st0 free
+    if (kt + 2 < nk) issue(st0, kt + 2);
+    compute(st1);
   }
+  __syncthreads();  // LDS free for the next tile of a persistent worker
 
   // Epilogue.  32x32 accumulator layout: lane holds column (lane & 31) and
   // rows 8*(r/4) + 4*(lane/32) + (r%4), r = 0..15.
