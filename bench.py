@@ -1,7 +1,7 @@
 """Throughput of the MoE expert layer (forward + backward) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
-                    [--unfused] [--no-cpu-baseline] [--cpu-tokens N]
+                    [--fused] [--no-cpu-baseline] [--cpu-tokens N]
 
 One step = one pass of the whole layer over one batch of synthetic, seeded
 inputs already resident in HBM: route (top-k, histogram, slot map) ->
@@ -40,9 +40,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral")
-    ap.add_argument("--unfused", action="store_true", help="time the unfused forward calls")
+    ap.add_argument("--fused", action="store_true",
+                    help="time the fused Dispatch+GEMM and GEMM+Combine entry points")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=128)
+    ap.add_argument("--cpu-tokens", type=int, default=384)
     ap.add_argument("--fwd-only", action="store_true")
     return ap.parse_args()
 
@@ -61,8 +62,10 @@ def algorithmic_work(d, b):
         "ffn_combine": ("mfma", gemm(RA, 1)),
         "combine": ("hbm", b * R * H + b * Ns * T * H + b * T * H + 8.0 * R),
         "combine_bwd": ("hbm", b * T * H + 2 * b * R * H + 12.0 * R),
-        "ffn_bwd_data": ("mfma", gemm(RA, 3)),
-        "ffn_bwd_weight": ("mfma", gemm(RA, 3)),
+        "ffn_bwd_act": ("mfma", gemm(RA, 1)),
+        "ffn_bwd_input": ("mfma", gemm(RA, 2)),
+        "ffn_bwd_wgrad_gate_up": ("mfma", gemm(RA, 2)),
+        "ffn_bwd_wgrad_down": ("mfma", gemm(RA, 1)),
         "dispatch_bwd": ("hbm", b * RA * H + b * T * H + 4.0 * R),
         "route_bwd": ("hbm", 12.0 * T * K + 4.0 * T * E),
     }
@@ -94,7 +97,7 @@ def main():
     d = L.make_dims(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.n_shared, cfg.dtype)
     b = L.Buffers(d, backward=backward)
     stream = torch.cuda.current_stream()
-    fused = not args.unfused
+    fused = args.fused
 
     calls = []  # (name, start_event, end_event)
 
@@ -123,16 +126,17 @@ def main():
         if backward:
             timed("combine_bwd", M.moe_combine_bwd, d, p["dout"], b.y, b.slot, b.topk_w, b.dy,
                   b.dtopk_w)
-            timed("ffn_bwd_data", M.moe_expert_ffn_bwd_data, d, b.dy, p.get("dout"), b.offsets,
-                  p["w1"], p["w3"], p["w2"], p.get("ws1"), p.get("ws3"), p.get("ws2"), b.ab,
-                  b.dab, b.dx_rows, b.ws)
-            timed("ffn_bwd_weight", M.moe_expert_ffn_bwd_weight, d, b.x_perm, p["x"], b.h, b.dy,
-                  p.get("dout"), b.dab, b.offsets, b.dw1, b.dw3, b.dw2, b.dws1, b.dws3, b.dws2,
-                  b.ws)
+            timed("ffn_bwd_act", M.moe_expert_ffn_bwd_act, d, b.dy, p.get("dout"), b.offsets,
+                  p["w2"], p.get("ws2"), b.ab, b.dab, b.ws)
+            timed("ffn_bwd_input", M.moe_expert_ffn_bwd_input, d, b.dab, b.offsets, p["w1"],
+                  p["w3"], p.get("ws1"), p.get("ws3"), b.dx_rows, b.ws)
+            timed("ffn_bwd_wgrad_gate_up", M.moe_expert_ffn_bwd_weight_gate_up, d, b.x_perm,
+                  p["x"], b.dab, b.offsets, b.dw1, b.dw3, b.dws1, b.dws3, b.ws)
+            timed("ffn_bwd_wgrad_down", M.moe_expert_ffn_bwd_weight_down, d, b.h, b.dy,
+                  p.get("dout"), b.offsets, b.dw2, b.dws2, b.ws)
             timed("dispatch_bwd", M.moe_dispatch_bwd, d, b.dx_rows, b.slot, b.dx)
             timed("route_bwd", M.moe_route_bwd, d, b.dtopk_w, b.topk_w, b.topk_idx, b.dlogits)
 
-    # a fused entry point that is not available falls back to nothing: fail loudly
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -19,7 +19,8 @@ __all__ = [
     "moe_last_error", "moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn_up",
     "moe_expert_ffn_down", "moe_expert_ffn", "moe_combine", "moe_dispatch_ffn",
     "moe_ffn_combine", "moe_combine_bwd", "moe_expert_ffn_bwd_data",
-    "moe_expert_ffn_bwd_weight", "moe_dispatch_bwd", "moe_route_bwd",
+    "moe_expert_ffn_bwd_weight", "moe_dispatch_bwd", "moe_route_bwd", "moe_expert_ffn_bwd_act",
+    "moe_expert_ffn_bwd_input", "moe_expert_ffn_bwd_weight_gate_up", "moe_expert_ffn_bwd_weight_down",
 ]
 
 F32, BF16 = 0, 1
@@ -78,6 +79,11 @@ _SIGS = {
                                                _P, ctypes.c_size_t, _P]),
     "moe_expert_ffn_bwd_weight": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                  _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_expert_ffn_bwd_act": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_expert_ffn_bwd_input": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_expert_ffn_bwd_weight_gate_up": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                         ctypes.c_size_t, _P]),
+    "moe_expert_ffn_bwd_weight_down": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_dispatch_bwd": (ctypes.c_int, [_D, _P, _P, _P, _P]),
     "moe_route_bwd": (ctypes.c_int, [_D, _P, _P, _P, _P, _P]),
 }
@@ -268,6 +274,48 @@ def moe_expert_ffn_bwd_weight(d: Dims, x_perm, x, h, dy, dout, dab, offsets, dw1
           _ptr(offsets, "offsets", torch.int32, E + 1), _ptr(dw1, "dw1", f32, E * H * I),
           _ptr(dw3, "dw3", f32, E * H * I), _ptr(dw2, "dw2", f32, E * I * H),
           _ptr(dws1, "dws1", f32, Ns * H * I), _ptr(dws3, "dws3", f32, Ns * H * I),
+          _ptr(dws2, "dws2", f32, Ns * I * H), wp, wn, _stream(stream))
+
+
+def moe_expert_ffn_bwd_act(d: Dims, dy, dout, offsets, w2, ws2, ab, dab, ws, stream=None):
+    dt, H, I, E, Ns = d.torch_dtype, d.H, d.I, d.E, d.n_shared
+    wp, wn = _ws(ws)
+    _call("moe_expert_ffn_bwd_act", ctypes.byref(d), _ptr(dy, "dy", dt, d.R * H),
+          _ptr(dout, "dout", dt, d.T * H), _ptr(offsets, "offsets", torch.int32, E + 1),
+          _ptr(w2, "w2", dt, E * I * H), _ptr(ws2, "ws2", dt, Ns * I * H),
+          _ptr(ab, "ab", dt, d.RA * 2 * I), _ptr(dab, "dab", dt, d.RA * 2 * I), wp, wn,
+          _stream(stream))
+
+
+def moe_expert_ffn_bwd_input(d: Dims, dab, offsets, w1, w3, ws1, ws3, dx_rows, ws, stream=None):
+    dt, H, I, E, Ns = d.torch_dtype, d.H, d.I, d.E, d.n_shared
+    wp, wn = _ws(ws)
+    _call("moe_expert_ffn_bwd_input", ctypes.byref(d), _ptr(dab, "dab", dt, d.RA * 2 * I),
+          _ptr(offsets, "offsets", torch.int32, E + 1), _ptr(w1, "w1", dt, E * H * I),
+          _ptr(w3, "w3", dt, E * H * I), _ptr(ws1, "ws1", dt, Ns * H * I),
+          _ptr(ws3, "ws3", dt, Ns * H * I), _ptr(dx_rows, "dx_rows", dt, d.RA * H), wp, wn,
+          _stream(stream))
+
+
+def moe_expert_ffn_bwd_weight_gate_up(d: Dims, x_perm, x, dab, offsets, dw1, dw3, dws1, dws3, ws,
+                                      stream=None):
+    dt, H, I, E, Ns = d.torch_dtype, d.H, d.I, d.E, d.n_shared
+    f32 = torch.float32
+    wp, wn = _ws(ws)
+    _call("moe_expert_ffn_bwd_weight_gate_up", ctypes.byref(d), _ptr(x_perm, "x_perm", dt, d.R * H),
+          _ptr(x, "x", dt, d.T * H), _ptr(dab, "dab", dt, d.RA * 2 * I),
+          _ptr(offsets, "offsets", torch.int32, E + 1), _ptr(dw1, "dw1", f32, E * H * I),
+          _ptr(dw3, "dw3", f32, E * H * I), _ptr(dws1, "dws1", f32, Ns * H * I),
+          _ptr(dws3, "dws3", f32, Ns * H * I), wp, wn, _stream(stream))
+
+
+def moe_expert_ffn_bwd_weight_down(d: Dims, h, dy, dout, offsets, dw2, dws2, ws, stream=None):
+    dt, H, I, E, Ns = d.torch_dtype, d.H, d.I, d.E, d.n_shared
+    f32 = torch.float32
+    wp, wn = _ws(ws)
+    _call("moe_expert_ffn_bwd_weight_down", ctypes.byref(d), _ptr(h, "h", dt, d.RA * I),
+          _ptr(dy, "dy", dt, d.R * H), _ptr(dout, "dout", dt, d.T * H),
+          _ptr(offsets, "offsets", torch.int32, E + 1), _ptr(dw2, "dw2", f32, E * I * H),
           _ptr(dws2, "dws2", f32, Ns * I * H), wp, wn, _stream(stream))
 
 

@@ -1,0 +1,178 @@
+// Fused persistent kernels: Dispatch+GroupGEMM and GroupGEMM+Combine.
+//
+// UniEP article, section 2.1/2.2: one launch per fused stage, a fixed set of
+// persistent workers, a single global atomic counter as the task cursor over
+// a linear task space -- the communication (here: gather) tasks first, the
+// GroupGEMM tiles after them -- and a scoreboard of per-tile readiness flags
+// in global memory that a compute task polls before it starts.  On one GPU the
+// "communication" of dispatch is the gather of token rows into the expert-
+// contiguous buffer, and the relay/arrival part of the scoreboard collapses to
+// one flag per GEMM row tile, set once all its rows are written.
+//
+// Deadlock freedom: a task only ever waits on tasks with smaller indices, and
+// every such task was claimed from the cursor by a worker that is running and
+// never waits itself (gather tasks, GEMM tiles of the combine kernel), so the
+// wait always ends, whatever the number of resident workers.
+//
+// Determinism: every GEMM tile runs the same tile code with the same operands
+// as the plain launch and every combine row the same combine code, so the
+// outputs are bit-identical to the unfused calls whatever order the workers
+// take the tasks in.
+#include "gemm_tile.hpp"
+#include "rows.hpp"
+
+namespace moe {
+
+__device__ __forceinline__ int claim_task(int32_t* cursor, int* slot) {
+  if (threadIdx.x == 0) *slot = atomicAdd(cursor, 1);
+  __syncthreads();
+  const int task = *slot;
+  __syncthreads();
+  return task;
+}
+
+// Every wave's global stores have reached L2, then one release publishes them.
+__device__ __forceinline__ void publish_set(int32_t* flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void publish_add(int32_t* counter) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+using UpCfg = BfPick<kUp>::C;
+using DownCfg = BfPick<kDown>::C;
+
+__global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
+                                                                  const int32_t* __restrict__ slot_src,
+                                                                  FusedWs w, int nt_count) {
+  using C = UpCfg;
+  __shared__ __align__(16) uint8_t st0[C::STAGE_BYTES];
+  __shared__ __align__(16) uint8_t st1[C::STAGE_BYTES];
+  __shared__ int task_slot;
+  const int n_mt = *w.n_mtiles;
+  const int total = n_mt + n_mt * nt_count;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int nvec = g.H / 8;
+  for (;;) {
+    const int task = claim_task(w.cursor, &task_slot);
+    if (task >= total) break;
+    if (task < n_mt) {
+      // gather task: x_perm rows of one row tile from their tokens
+      const int4 mt = w.mtiles[task];
+      if (mt.x < g.E) {
+        const uint16_t* x = static_cast<const uint16_t*>(g.x);
+        uint16_t* xp = static_cast<uint16_t*>(g.o_x_perm);
+        for (int r = wave; r < mt.z; r += C::NW) {
+          const int64_t s = mt.y + r;
+          const char* src = reinterpret_cast<const char*>(x + (int64_t)slot_src[s] * g.H);
+          char* dst = reinterpret_cast<char*>(xp + s * g.H);
+          for (int v = lane; v < nvec; v += kWave) st16(dst + (int64_t)v * 16, ld16(src + (int64_t)v * 16));
+        }
+      }
+      publish_set(&w.flags[task]);
+    } else {
+      int tm, tn;
+      band_order(task - n_mt, n_mt, nt_count, tm, tn);
+      if (threadIdx.x == 0)
+        while (__hip_atomic_load(&w.flags[tm], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0)
+          __builtin_amdgcn_s_sleep(2);
+      __syncthreads();
+      const TileDesc<uint16_t> d = decode_tile<uint16_t, kUp, C::BM, C::BN>(g, tm, tn);
+      run_tile_bf16<C>(g, d, st0, st1);
+    }
+  }
+}
+
+// Row tile of all-rows index `row`: the group from the expert offsets (or the
+// shared block), then the tile inside the group.
+__device__ __forceinline__ int tile_of_row(int64_t row, const GemmArgs& g, const int32_t* first_tile,
+                                          int bm) {
+  if (row >= g.R) {
+    const int64_t sh = (row - g.R) / g.T;
+    return first_tile[g.E + sh] + (int)((row - g.R - sh * g.T) / bm);
+  }
+  int lo = 0, hi = g.E;  // largest e with offsets[e] <= row
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (g.offsets[mid] <= row) lo = mid; else hi = mid;
+  }
+  return first_tile[lo] + (int)((row - g.offsets[lo]) / bm);
+}
+
+constexpr int kCombineTokens = 16;  // tokens per combine task
+
+__global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
+                                                                   const int32_t* __restrict__ slot,
+                                                                   const float* __restrict__ topk_w,
+                                                                   FusedWs w, int nt_count) {
+  using C = DownCfg;
+  __shared__ __align__(16) uint8_t st0[C::STAGE_BYTES];
+  __shared__ __align__(16) uint8_t st1[C::STAGE_BYTES];
+  __shared__ int task_slot;
+  const int n_mt = *w.n_mtiles;
+  const int n_gemm = n_mt * nt_count;
+  const int n_comb = (g.T + kCombineTokens - 1) / kCombineTokens;
+  const int total = n_gemm + n_comb;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  for (;;) {
+    const int task = claim_task(w.cursor, &task_slot);
+    if (task >= total) break;
+    if (task < n_gemm) {
+      int tm, tn;
+      band_order(task, n_mt, nt_count, tm, tn);
+      const TileDesc<uint16_t> d = decode_tile<uint16_t, kDown, C::BM, C::BN>(g, tm, tn);
+      run_tile_bf16<C>(g, d, st0, st1);
+      publish_add(&w.flags[tm]);
+    } else {
+      const int t0 = (task - n_gemm) * kCombineTokens;
+      const int t1 = min(g.T, t0 + kCombineTokens);
+      for (int t = t0 + wave; t < t1; t += C::NW) {
+        // the row tiles holding the token's routed rows (q < K) and its
+        // shared-expert rows (q >= K) must all be complete
+        for (int q = lane; q < g.K + g.Ns; q += kWave) {
+          const int64_t row = q < g.K ? (int64_t)slot[(int64_t)t * g.K + q]
+                                      : g.R + (int64_t)(q - g.K) * g.T + t;
+          const int tile = tile_of_row(row, g, w.first_tile, C::BM);
+          while (__hip_atomic_load(&w.flags[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nt_count)
+            __builtin_amdgcn_s_sleep(2);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        combine_row<uint16_t>(static_cast<const uint16_t*>(g.o_y), slot, topk_w,
+                              static_cast<uint16_t*>(g.o_out), t, g.T, g.H, g.K, g.Ns, lane);
+      }
+    }
+  }
+}
+
+hipError_t launch_dispatch_ffn(const GemmArgs& a0, const int32_t* slot_src, const FusedWs& w,
+                               hipStream_t st) {
+  GemmArgs a = a0;
+  a.mtiles = w.mtiles;
+  a.n_mtiles = w.n_mtiles;
+  hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, UpCfg::BM, w.mtiles, w.n_mtiles,
+                             w.first_tile, w.flags, w.mt_bound + 1, st);
+  if (e != hipSuccess) return e;
+  const int nt = gemm_ntiles<kUp>(a.H, a.I, UpCfg::BN);
+  dispatch_ffn_kernel<<<w.workers, UpCfg::NT, 0, st>>>(a, slot_src, w, nt);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_combine(const GemmArgs& a0, const int32_t* slot, const float* topk_w,
+                              const FusedWs& w, hipStream_t st) {
+  GemmArgs a = a0;
+  a.mtiles = w.mtiles;
+  a.n_mtiles = w.n_mtiles;
+  hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, DownCfg::BM, w.mtiles, w.n_mtiles,
+                             w.first_tile, w.flags, w.mt_bound + 1, st);
+  if (e != hipSuccess) return e;
+  const int nt = gemm_ntiles<kDown>(a.H, a.I, DownCfg::BN);
+  ffn_combine_kernel<<<w.workers, DownCfg::NT, 0, st>>>(a, slot, topk_w, w, nt);
+  return hipGetLastError();
+}
+
+}  // namespace moe

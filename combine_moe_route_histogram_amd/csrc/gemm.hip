@@ -17,7 +17,9 @@ namespace moe {
 __global__ __launch_bounds__(64) void plan_mtiles_kernel(const int32_t* __restrict__ offsets, int E,
                                                          int Ns, int T, int R, int bm,
                                                          int4* __restrict__ mtiles,
-                                                         int32_t* __restrict__ n_mtiles) {
+                                                         int32_t* __restrict__ n_mtiles,
+                                                         int32_t* __restrict__ first_tile,
+                                                         int32_t* __restrict__ clear, int n_clear) {
   const int lane = threadIdx.x;
   const int G = E + Ns;
   const int per = (G + kWave - 1) / kWave;
@@ -47,9 +49,19 @@ __global__ __launch_bounds__(64) void plan_mtiles_kernel(const int32_t* __restri
   for (int grp = g_begin; grp < g_end; ++grp) {
     int row0, rows;
     group_rows(grp, row0, rows);
+    if (first_tile) first_tile[grp] = idx;
     for (int r = 0; r < rows; r += bm) mtiles[idx++] = make_int4(grp, row0 + r, min(bm, rows - r), 0);
   }
   if (lane == kWave - 1) *n_mtiles = incl;
+  for (int i = lane; i < n_clear; i += kWave) clear[i] = 0;
+}
+
+hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int bm, int4* mtiles,
+                       int32_t* n_mtiles, int32_t* first_tile, int32_t* clear, int n_clear,
+                       hipStream_t st) {
+  plan_mtiles_kernel<<<1, 64, 0, st>>>(offsets, E, Ns, T, R, bm, mtiles, n_mtiles, first_tile,
+                                       clear, n_clear);
+  return hipGetLastError();
 }
 
 // Launch order -> logical tile.  Workgroups are handed to the 8 XCDs round
@@ -58,20 +70,6 @@ __global__ __launch_bounds__(64) void plan_mtiles_kernel(const int32_t* __restri
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   if (nblocks % 8) return bid;
   return (bid % 8) * (nblocks / 8) + bid / 8;
-}
-
-// Logical tile -> (row tile, column tile).  Row tiles are taken in bands of
-// kBandM; inside a band the column tiles advance slowest, so the tiles an XCD
-// runs at the same time form a kBandM x (concurrent / kBandM) block: each
-// operand slice they load is shared by several of them through L2.
-constexpr int kBandM = 8;
-__device__ __forceinline__ void band_order(int L, int mt_count, int nt_count, int& tm, int& tn) {
-  const int band_tiles = kBandM * nt_count;
-  const int band = L / band_tiles;
-  const int rem = L - band * band_tiles;
-  const int rows = min(kBandM, mt_count - band * kBandM);
-  tn = rem / rows;
-  tm = band * kBandM + (rem - tn * rows);
 }
 
 template <class C>
@@ -98,33 +96,6 @@ __global__ __launch_bounds__(kF32NT) void gemm_f32_kernel(GemmArgs g, int mt_cou
   run_tile_f32<KIND>(g, d, smem_f);
 }
 
-// bf16 tile configurations per kind: BM, BN, waves along M, waves along N.
-#ifndef MOE_CFG_UP
-#define MOE_CFG_UP 128, 256, 2, 2, 2
-#endif
-#ifndef MOE_CFG_DOWN
-#define MOE_CFG_DOWN 128, 256, 2, 2, 2
-#endif
-#ifndef MOE_CFG_BWD_UP
-#define MOE_CFG_BWD_UP 128, 256, 2, 2, 2
-#endif
-#ifndef MOE_CFG_BWD_DOWN
-#define MOE_CFG_BWD_DOWN 128, 256, 2, 2, 2
-#endif
-#ifndef MOE_CFG_WG_UP
-#define MOE_CFG_WG_UP 128, 256, 2, 2, 2
-#endif
-#ifndef MOE_CFG_WG_DOWN
-#define MOE_CFG_WG_DOWN 128, 256, 2, 2, 2
-#endif
-template <int KIND> struct BfPick;
-template <> struct BfPick<kUp> { using C = BfCfg<kUp, MOE_CFG_UP>; };
-template <> struct BfPick<kDown> { using C = BfCfg<kDown, MOE_CFG_DOWN>; };
-template <> struct BfPick<kBwdUp> { using C = BfCfg<kBwdUp, MOE_CFG_BWD_UP>; };
-template <> struct BfPick<kBwdDown> { using C = BfCfg<kBwdDown, MOE_CFG_BWD_DOWN>; };
-template <> struct BfPick<kWgUp> { using C = BfCfg<kWgUp, MOE_CFG_WG_UP>; };
-template <> struct BfPick<kWgDown> { using C = BfCfg<kWgDown, MOE_CFG_WG_DOWN>; };
-
 template <int KIND>
 static hipError_t launch_kind(bool is_bf16, GemmArgs a, int4* mtiles_ws, int32_t* n_ws,
                               hipStream_t st) {
@@ -133,7 +104,8 @@ static hipError_t launch_kind(bool is_bf16, GemmArgs a, int4* mtiles_ws, int32_t
   const int BN = is_bf16 ? C::BN : kF32BN;
   int mt_count;
   if constexpr (!KindTraits<KIND>::kWgrad) {
-    plan_mtiles_kernel<<<1, 64, 0, st>>>(a.offsets, a.E, a.Ns, a.T, a.R, BM, mtiles_ws, n_ws);
+    plan_mtiles_kernel<<<1, 64, 0, st>>>(a.offsets, a.E, a.Ns, a.T, a.R, BM, mtiles_ws, n_ws,
+                                         nullptr, nullptr, 0);
     a.mtiles = mtiles_ws;
     a.n_mtiles = n_ws;
     mt_count = (int)mtile_bound(a.T, a.K, a.E, a.Ns, BM);

@@ -583,4 +583,48 @@ __device__ void run_tile_f32(const GemmArgs& g, const TileDesc<float>& d, float*
 
 constexpr int kF32LdsFloats = kF32BK * (kF32BM + 4) + kF32BK * (kF32BN + 4);
 
+// Logical tile -> (row tile, column tile).  Row tiles are taken in bands of
+// kBandM; inside a band the column tiles advance slowest, so the tiles an XCD
+// runs at the same time form a kBandM x (concurrent / kBandM) block: each
+// operand slice they load is shared by several of them through L2.
+constexpr int kBandM = 8;
+__device__ __forceinline__ void band_order(int L, int mt_count, int nt_count, int& tm, int& tn) {
+  const int band_tiles = kBandM * nt_count;
+  const int band = L / band_tiles;
+  const int rem = L - band * band_tiles;
+  const int rows = min(kBandM, mt_count - band * kBandM);
+  tn = rem / rows;
+  tm = band * kBandM + (rem - tn * rows);
+}
+
+// bf16 tile configurations per kind: BM, BN, waves along M, waves along N,
+// LDS k slices.  The fused kernels use the same ones, so their tiles are
+// computed exactly as by the plain launches.
+#ifndef MOE_CFG_UP
+#define MOE_CFG_UP 128, 256, 2, 2, 2
+#endif
+#ifndef MOE_CFG_DOWN
+#define MOE_CFG_DOWN 128, 256, 2, 2, 2
+#endif
+#ifndef MOE_CFG_BWD_UP
+#define MOE_CFG_BWD_UP 128, 256, 2, 2, 2
+#endif
+#ifndef MOE_CFG_BWD_DOWN
+#define MOE_CFG_BWD_DOWN 128, 256, 2, 2, 2
+#endif
+#ifndef MOE_CFG_WG_UP
+#define MOE_CFG_WG_UP 128, 256, 2, 2, 2
+#endif
+#ifndef MOE_CFG_WG_DOWN
+#define MOE_CFG_WG_DOWN 128, 256, 2, 2, 2
+#endif
+template <int KIND> struct BfPick;
+template <> struct BfPick<kUp> { using C = BfCfg<kUp, MOE_CFG_UP>; };
+template <> struct BfPick<kDown> { using C = BfCfg<kDown, MOE_CFG_DOWN>; };
+template <> struct BfPick<kBwdUp> { using C = BfCfg<kBwdUp, MOE_CFG_BWD_UP>; };
+template <> struct BfPick<kBwdDown> { using C = BfCfg<kBwdDown, MOE_CFG_BWD_DOWN>; };
+template <> struct BfPick<kWgUp> { using C = BfCfg<kWgUp, MOE_CFG_WG_UP>; };
+template <> struct BfPick<kWgDown> { using C = BfCfg<kWgDown, MOE_CFG_WG_DOWN>; };
+
+
 }  // namespace moe

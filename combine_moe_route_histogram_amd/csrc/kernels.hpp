@@ -18,6 +18,8 @@ hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* topk_
 // Row kernels; is_bf16 selects the storage type (bf16 or f32).
 hipError_t launch_dispatch(bool is_bf16, const void* x, const int32_t* slot, void* x_perm, int T,
                            int H, int K, hipStream_t st);
+hipError_t launch_gather(bool is_bf16, const void* x, const int32_t* slot_src, void* x_perm,
+                         int64_t R, int H, hipStream_t st);
 hipError_t launch_combine(bool is_bf16, const void* y, const int32_t* slot, const float* w,
                           void* out, int T, int H, int K, int Ns, hipStream_t st);
 hipError_t launch_combine_bwd(bool is_bf16, const void* dout, const void* y, const int32_t* slot,
@@ -57,6 +59,8 @@ struct GemmArgs {
   const void* dy;
   const void* dout;
   const void* dab;
+  void* o_x_perm;  // fused dispatch: gather target (same buffer as x_perm)
+  void* o_out;     // fused combine: token outputs
   void* o_ab;
   void* o_h;
   void* o_y;
@@ -81,5 +85,27 @@ constexpr int kMinTileM = 64;
 
 hipError_t launch_gemm(bool is_bf16, int kind, const GemmArgs& a, int4* mtiles_ws,
                        int32_t* n_mtiles_ws, hipStream_t st);
+
+// Row-tile planner (one wave): table of bm-row tiles per group, the first
+// table index of every group (if first_tile), and n_clear ints of `clear` set
+// to zero (flags and cursors of the fused kernels).
+hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int bm, int4* mtiles,
+                       int32_t* n_mtiles, int32_t* first_tile, int32_t* clear, int n_clear,
+                       hipStream_t st);
+
+// Fused persistent kernels (bf16).  ws_* are workspace sections.
+struct FusedWs {
+  int4* mtiles;
+  int32_t* n_mtiles;
+  int32_t* first_tile;  // [E + Ns]
+  int32_t* flags;       // [mt bound]: ready (dispatch_ffn) or done counters (ffn_combine)
+  int32_t* cursor;      // [1]
+  int mt_bound;
+  int workers;          // persistent workgroups to launch
+};
+hipError_t launch_dispatch_ffn(const GemmArgs& a, const int32_t* slot_src, const FusedWs& w,
+                               hipStream_t st);
+hipError_t launch_ffn_combine(const GemmArgs& a, const int32_t* slot, const float* topk_w,
+                              const FusedWs& w, hipStream_t st);
 
 }  // namespace moe

@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 
@@ -37,7 +38,8 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace sections (byte offsets).
 struct Layout {
-  size_t chunk_counts, chunk_base, mtiles, n_mtiles, ready, done, cursor, total;
+  size_t chunk_counts, chunk_base, mtiles, n_mtiles, first_tile, flags, total;
+  int mt_bound;
 };
 
 Layout layout(const moe_dims* d) {
@@ -49,10 +51,10 @@ Layout layout(const moe_dims* d) {
   L.chunk_base = off;   off = align_up(off + nchunk * d->E * 4);
   L.mtiles = off;       off = align_up(off + mt * 16);
   L.n_mtiles = off;     off = align_up(off + 16);
-  L.ready = off;        off = align_up(off + mt * 4);
-  L.done = off;         off = align_up(off + mt * 4);
-  L.cursor = off;       off = align_up(off + 64);
+  L.first_tile = off;   off = align_up(off + (size_t)(d->E + d->n_shared) * 4);
+  L.flags = off;        off = align_up(off + (mt + 1) * 4);  // flags, then the task cursor
   L.total = off;
+  L.mt_bound = (int)mt;
   return L;
 }
 
@@ -124,6 +126,42 @@ struct DeviceCache {
 };
 DeviceCache g_dev;
 
+// CU count of the current device (cached).
+int current_cu_count(int* out) {
+  int dev = 0;
+  MOE_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= 64) return fail(MOE_EINVAL, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev.mu);
+  if (!g_dev.cu_count[dev]) {
+    int n = 0;
+    MOE_TRY(hip_status(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev),
+                       "hipDeviceGetAttribute"));
+    g_dev.cu_count[dev] = n;
+  }
+  *out = g_dev.cu_count[dev];
+  return MOE_OK;
+}
+
+// Workspace sections of the fused kernels; one persistent worker per CU
+// (each uses most of a CU's LDS).
+int fused_ws(const moe_dims* d, void* ws, FusedWs* w) {
+  const Layout L = layout(d);
+  w->mtiles = ws_at<int4>(ws, L.mtiles);
+  w->n_mtiles = ws_at<int32_t>(ws, L.n_mtiles);
+  w->first_tile = ws_at<int32_t>(ws, L.first_tile);
+  w->flags = ws_at<int32_t>(ws, L.flags);
+  w->cursor = w->flags + L.mt_bound;
+  w->mt_bound = L.mt_bound;
+  MOE_TRY(current_cu_count(&w->workers));
+  // MOE_FUSED_WORKERS (debug): launch this many persistent workers instead,
+  // to check that results do not depend on how many workers share the tasks.
+  if (const char* e = getenv("MOE_FUSED_WORKERS")) {
+    const int n = atoi(e);
+    if (n > 0) w->workers = n;
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -132,9 +170,10 @@ int moe_init(int device) {
   if (device < 0 || device >= 64) return fail(MOE_EINVAL, "device index %d out of range", device);
   std::lock_guard<std::mutex> lk(g_dev.mu);
   if (g_dev.cu_count[device]) return MOE_OK;
-  hipDeviceProp_t p;
-  MOE_TRY(hip_status(hipGetDeviceProperties(&p, device), "hipGetDeviceProperties"));
-  g_dev.cu_count[device] = p.multiProcessorCount;
+  int n = 0;
+  MOE_TRY(hip_status(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device),
+                     "hipDeviceGetAttribute"));
+  g_dev.cu_count[device] = n;
   return MOE_OK;
 }
 
@@ -245,17 +284,60 @@ int moe_dispatch_ffn(const moe_dims* d, const void* x, const int32_t* slot_src,
                      const int32_t* offsets, const void* w1, const void* w3, const void* ws1,
                      const void* ws3, void* x_perm, void* ab, void* h, void* ws, size_t ws_bytes,
                      void* stream) {
-  (void)d; (void)x; (void)slot_src; (void)offsets; (void)w1; (void)w3; (void)ws1; (void)ws3;
-  (void)x_perm; (void)ab; (void)h; (void)ws; (void)ws_bytes; (void)stream;
-  return fail(MOE_EUNSUPPORTED, "moe_dispatch_ffn: not built yet");
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_ptr(x, "x"));
+  MOE_TRY(check_ptr(slot_src, "slot_src"));
+  MOE_TRY(check_ptr(offsets, "offsets"));
+  MOE_TRY(check_ptr(w1, "w1"));
+  MOE_TRY(check_ptr(w3, "w3"));
+  MOE_TRY(check_ptr(x_perm, "x_perm"));
+  MOE_TRY(check_ptr(ab, "ab"));
+  MOE_TRY(check_ptr(h, "h"));
+  if (d->n_shared) {
+    MOE_TRY(check_ptr(ws1, "ws1"));
+    MOE_TRY(check_ptr(ws3, "ws3"));
+  }
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  const hipStream_t st = as_stream(stream);
+  if (d->dtype != MOE_BF16) {
+    // f32 has no persistent kernel: a plain gather and the plain GEMM launch
+    // give the same result
+    MOE_TRY(hip_status(launch_gather(false, x, slot_src, x_perm, d->T * d->K, d->H, st),
+                       "moe_dispatch_ffn (gather)"));
+    return moe_expert_ffn_up(d, x_perm, x, offsets, w1, w3, ws1, ws3, ab, h, ws, ws_bytes, stream);
+  }
+  GemmArgs a = base_args(d, offsets);
+  a.x_perm = x_perm; a.o_x_perm = x_perm; a.x = x; a.w1 = w1; a.w3 = w3; a.ws1 = ws1; a.ws3 = ws3;
+  a.o_ab = ab; a.o_h = h;
+  FusedWs w;
+  MOE_TRY(fused_ws(d, ws, &w));
+  return hip_status(launch_dispatch_ffn(a, slot_src, w, st), "moe_dispatch_ffn");
 }
 
 int moe_ffn_combine(const moe_dims* d, const void* h, const int32_t* offsets, const void* w2,
                     const void* ws2, const int32_t* slot, const float* topk_w, void* y, void* out,
                     void* ws, size_t ws_bytes, void* stream) {
-  (void)d; (void)h; (void)offsets; (void)w2; (void)ws2; (void)slot; (void)topk_w; (void)y;
-  (void)out; (void)ws; (void)ws_bytes; (void)stream;
-  return fail(MOE_EUNSUPPORTED, "moe_ffn_combine: not built yet");
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_ptr(h, "h"));
+  MOE_TRY(check_ptr(offsets, "offsets"));
+  MOE_TRY(check_ptr(w2, "w2"));
+  MOE_TRY(check_ptr(slot, "slot"));
+  MOE_TRY(check_ptr(topk_w, "topk_w"));
+  MOE_TRY(check_ptr(y, "y"));
+  MOE_TRY(check_ptr(out, "out"));
+  if (d->n_shared) MOE_TRY(check_ptr(ws2, "ws2"));
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  const hipStream_t st = as_stream(stream);
+  if (d->dtype != MOE_BF16) {
+    // f32 has no persistent kernel: the two plain launches give the same result
+    MOE_TRY(moe_expert_ffn_down(d, h, offsets, w2, ws2, y, ws, ws_bytes, stream));
+    return moe_combine(d, y, slot, topk_w, out, stream);
+  }
+  GemmArgs a = base_args(d, offsets);
+  a.h = h; a.w2 = w2; a.ws2 = ws2; a.o_y = y; a.o_out = out;
+  FusedWs w;
+  MOE_TRY(fused_ws(d, ws, &w));
+  return hip_status(launch_ffn_combine(a, slot, topk_w, w, st), "moe_ffn_combine");
 }
 
 int moe_combine_bwd(const moe_dims* d, const void* dout, const void* y, const int32_t* slot,
@@ -272,33 +354,91 @@ int moe_combine_bwd(const moe_dims* d, const void* dout, const void* y, const in
                     "moe_combine_bwd");
 }
 
+int moe_expert_ffn_bwd_act(const moe_dims* d, const void* dy, const void* dout,
+                           const int32_t* offsets, const void* w2, const void* ws2,
+                           const void* ab, void* dab, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_ptr(dy, "dy"));
+  MOE_TRY(check_ptr(offsets, "offsets"));
+  MOE_TRY(check_ptr(w2, "w2"));
+  MOE_TRY(check_ptr(ab, "ab"));
+  MOE_TRY(check_ptr(dab, "dab"));
+  if (d->n_shared) {
+    MOE_TRY(check_ptr(dout, "dout"));
+    MOE_TRY(check_ptr(ws2, "ws2"));
+  }
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  GemmArgs a = base_args(d, offsets);
+  a.dy = dy; a.dout = dout; a.w2 = w2; a.ws2 = ws2; a.ab = ab; a.o_dab = dab;
+  return gemm(d, kBwdUp, a, ws, as_stream(stream), "moe_expert_ffn_bwd_act");
+}
+
+int moe_expert_ffn_bwd_input(const moe_dims* d, const void* dab, const int32_t* offsets,
+                             const void* w1, const void* w3, const void* ws1, const void* ws3,
+                             void* dx_rows, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_ptr(dab, "dab"));
+  MOE_TRY(check_ptr(offsets, "offsets"));
+  MOE_TRY(check_ptr(w1, "w1"));
+  MOE_TRY(check_ptr(w3, "w3"));
+  MOE_TRY(check_ptr(dx_rows, "dx_rows"));
+  if (d->n_shared) {
+    MOE_TRY(check_ptr(ws1, "ws1"));
+    MOE_TRY(check_ptr(ws3, "ws3"));
+  }
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  GemmArgs a = base_args(d, offsets);
+  a.dab = dab; a.w1 = w1; a.w3 = w3; a.ws1 = ws1; a.ws3 = ws3; a.o_dx = dx_rows;
+  return gemm(d, kBwdDown, a, ws, as_stream(stream), "moe_expert_ffn_bwd_input");
+}
+
 int moe_expert_ffn_bwd_data(const moe_dims* d, const void* dy, const void* dout,
                             const int32_t* offsets, const void* w1, const void* w3,
                             const void* w2, const void* ws1, const void* ws3, const void* ws2,
                             const void* ab, void* dab, void* dx_rows, void* ws, size_t ws_bytes,
                             void* stream) {
+  MOE_TRY(moe_expert_ffn_bwd_act(d, dy, dout, offsets, w2, ws2, ab, dab, ws, ws_bytes, stream));
+  return moe_expert_ffn_bwd_input(d, dab, offsets, w1, w3, ws1, ws3, dx_rows, ws, ws_bytes, stream);
+}
+
+int moe_expert_ffn_bwd_weight_gate_up(const moe_dims* d, const void* x_perm, const void* x,
+                                      const void* dab, const int32_t* offsets, float* dw1,
+                                      float* dw3, float* dws1, float* dws3, void* ws,
+                                      size_t ws_bytes, void* stream) {
   MOE_TRY(check_dims(d));
-  MOE_TRY(check_ptr(dy, "dy"));
-  MOE_TRY(check_ptr(offsets, "offsets"));
-  MOE_TRY(check_ptr(w1, "w1"));
-  MOE_TRY(check_ptr(w3, "w3"));
-  MOE_TRY(check_ptr(w2, "w2"));
-  MOE_TRY(check_ptr(ab, "ab"));
+  MOE_TRY(check_ptr(x_perm, "x_perm"));
   MOE_TRY(check_ptr(dab, "dab"));
-  MOE_TRY(check_ptr(dx_rows, "dx_rows"));
+  MOE_TRY(check_ptr(offsets, "offsets"));
+  MOE_TRY(check_ptr(dw1, "dw1"));
+  MOE_TRY(check_ptr(dw3, "dw3"));
   if (d->n_shared) {
-    MOE_TRY(check_ptr(dout, "dout"));
-    MOE_TRY(check_ptr(ws1, "ws1"));
-    MOE_TRY(check_ptr(ws3, "ws3"));
-    MOE_TRY(check_ptr(ws2, "ws2"));
+    MOE_TRY(check_ptr(x, "x"));
+    MOE_TRY(check_ptr(dws1, "dws1"));
+    MOE_TRY(check_ptr(dws3, "dws3"));
   }
   MOE_TRY(check_ws(d, ws, ws_bytes));
-  const hipStream_t st = as_stream(stream);
   GemmArgs a = base_args(d, offsets);
-  a.dy = dy; a.dout = dout; a.w1 = w1; a.w3 = w3; a.w2 = w2; a.ws1 = ws1; a.ws3 = ws3; a.ws2 = ws2;
-  a.ab = ab; a.o_dab = dab; a.dab = dab; a.o_dx = dx_rows;
-  MOE_TRY(gemm(d, kBwdUp, a, ws, st, "moe_expert_ffn_bwd_data (dh)"));
-  return gemm(d, kBwdDown, a, ws, st, "moe_expert_ffn_bwd_data (dx)");
+  a.x_perm = x_perm; a.x = x; a.dab = dab;
+  a.o_dw1 = dw1; a.o_dw3 = dw3; a.o_dws1 = dws1; a.o_dws3 = dws3;
+  return gemm(d, kWgUp, a, ws, as_stream(stream), "moe_expert_ffn_bwd_weight_gate_up");
+}
+
+int moe_expert_ffn_bwd_weight_down(const moe_dims* d, const void* h, const void* dy,
+                                   const void* dout, const int32_t* offsets, float* dw2,
+                                   float* dws2, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_ptr(h, "h"));
+  MOE_TRY(check_ptr(dy, "dy"));
+  MOE_TRY(check_ptr(offsets, "offsets"));
+  MOE_TRY(check_ptr(dw2, "dw2"));
+  if (d->n_shared) {
+    MOE_TRY(check_ptr(dout, "dout"));
+    MOE_TRY(check_ptr(dws2, "dws2"));
+  }
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  GemmArgs a = base_args(d, offsets);
+  a.h = h; a.dy = dy; a.dout = dout; a.o_dw2 = dw2; a.o_dws2 = dws2;
+  return gemm(d, kWgDown, a, ws, as_stream(stream), "moe_expert_ffn_bwd_weight_down");
 }
 
 int moe_expert_ffn_bwd_weight(const moe_dims* d, const void* x_perm, const void* x,
@@ -306,29 +446,9 @@ int moe_expert_ffn_bwd_weight(const moe_dims* d, const void* x_perm, const void*
                               const int32_t* offsets, float* dw1, float* dw3, float* dw2,
                               float* dws1, float* dws3, float* dws2, void* ws, size_t ws_bytes,
                               void* stream) {
-  MOE_TRY(check_dims(d));
-  MOE_TRY(check_ptr(x_perm, "x_perm"));
-  MOE_TRY(check_ptr(h, "h"));
-  MOE_TRY(check_ptr(dy, "dy"));
-  MOE_TRY(check_ptr(dab, "dab"));
-  MOE_TRY(check_ptr(offsets, "offsets"));
-  MOE_TRY(check_ptr(dw1, "dw1"));
-  MOE_TRY(check_ptr(dw3, "dw3"));
-  MOE_TRY(check_ptr(dw2, "dw2"));
-  if (d->n_shared) {
-    MOE_TRY(check_ptr(x, "x"));
-    MOE_TRY(check_ptr(dout, "dout"));
-    MOE_TRY(check_ptr(dws1, "dws1"));
-    MOE_TRY(check_ptr(dws3, "dws3"));
-    MOE_TRY(check_ptr(dws2, "dws2"));
-  }
-  MOE_TRY(check_ws(d, ws, ws_bytes));
-  const hipStream_t st = as_stream(stream);
-  GemmArgs a = base_args(d, offsets);
-  a.x_perm = x_perm; a.x = x; a.h = h; a.dy = dy; a.dout = dout; a.dab = dab;
-  a.o_dw1 = dw1; a.o_dw3 = dw3; a.o_dw2 = dw2; a.o_dws1 = dws1; a.o_dws3 = dws3; a.o_dws2 = dws2;
-  MOE_TRY(gemm(d, kWgUp, a, ws, st, "moe_expert_ffn_bwd_weight (dW1, dW3)"));
-  return gemm(d, kWgDown, a, ws, st, "moe_expert_ffn_bwd_weight (dW2)");
+  MOE_TRY(moe_expert_ffn_bwd_weight_gate_up(d, x_perm, x, dab, offsets, dw1, dw3, dws1, dws3, ws,
+                                            ws_bytes, stream));
+  return moe_expert_ffn_bwd_weight_down(d, h, dy, dout, offsets, dw2, dws2, ws, ws_bytes, stream);
 }
 
 int moe_dispatch_bwd(const moe_dims* d, const void* dx_rows, const int32_t* slot, void* dx,

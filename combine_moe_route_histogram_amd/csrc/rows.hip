@@ -9,6 +9,7 @@
 // (combine); the backward mirrors the forward.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "rows.hpp"
 
 namespace moe {
 
@@ -46,37 +47,18 @@ __global__ __launch_bounds__(kRowBlock) void dispatch_kernel(const S* __restrict
   }
 }
 
-// out[t] = sum_k w[t,k] y[slot[t,k]] + sum_s y[R + s*T + t]; one rounding.
+// x_perm[s] = x[slot_src[s]]: the same rows as dispatch, indexed by destination.
 template <typename S>
-__device__ __forceinline__ void combine_row(const S* __restrict__ y, const int32_t* __restrict__ slot,
-                                            const float* __restrict__ w, S* __restrict__ out,
-                                            int t, int T, int H, int K, int Ns, int lane) {
-  constexpr int P = Elem<S>::kPerVec;
-  const int my_slot = lane < K ? slot[(int64_t)t * K + lane] : 0;
-  const float my_w = lane < K ? w[(int64_t)t * K + lane] : 0.f;
-  const int64_t R = (int64_t)T * K;
-  const int nvec = H / P;
-  for (int v = lane; v < nvec; v += kWave) {
-    float acc[P];
-#pragma unroll
-    for (int j = 0; j < P; ++j) acc[j] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int s = __shfl(my_slot, k, kWave);
-      const float wk = __shfl(my_w, k, kWave);
-      float f[P];
-      Elem<S>::unpack(ld16(reinterpret_cast<const char*>(y + (int64_t)s * H) + (int64_t)v * 16), f);
-#pragma unroll
-      for (int j = 0; j < P; ++j) acc[j] = fmaf(wk, f[j], acc[j]);
-    }
-    for (int sh = 0; sh < Ns; ++sh) {
-      float f[P];
-      Elem<S>::unpack(ld16(reinterpret_cast<const char*>(y + (R + (int64_t)sh * T + t) * H) +
-                           (int64_t)v * 16), f);
-#pragma unroll
-      for (int j = 0; j < P; ++j) acc[j] += f[j];
-    }
-    st16(reinterpret_cast<char*>(out + (int64_t)t * H) + (int64_t)v * 16, Elem<S>::pack(acc));
-  }
+__global__ __launch_bounds__(kRowBlock) void gather_kernel(const S* __restrict__ x,
+                                                           const int32_t* __restrict__ slot_src,
+                                                           S* __restrict__ x_perm, int64_t R, int H) {
+  const int64_t s = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (s >= R) return;
+  const char* src = reinterpret_cast<const char*>(x + (int64_t)slot_src[s] * H);
+  char* dst = reinterpret_cast<char*>(x_perm + s * H);
+  const int nvec = H / Elem<S>::kPerVec;
+  for (int v = lane; v < nvec; v += kWave) st16(dst + (int64_t)v * 16, ld16(src + (int64_t)v * 16));
 }
 
 template <typename S>
@@ -203,6 +185,18 @@ hipError_t launch_dispatch(bool is_bf16, const void* x, const int32_t* slot, voi
   else
     dispatch_kernel<float><<<row_grid(T), kRowBlock, 0, st>>>(
         static_cast<const float*>(x), slot, static_cast<float*>(x_perm), T, H, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(bool is_bf16, const void* x, const int32_t* slot_src, void* x_perm,
+                         int64_t R, int H, hipStream_t st) {
+  const dim3 grid((unsigned)((R + kRowsPerBlock - 1) / kRowsPerBlock));
+  if (is_bf16)
+    gather_kernel<uint16_t><<<grid, kRowBlock, 0, st>>>(static_cast<const uint16_t*>(x), slot_src,
+                                                        static_cast<uint16_t*>(x_perm), R, H);
+  else
+    gather_kernel<float><<<grid, kRowBlock, 0, st>>>(static_cast<const float*>(x), slot_src,
+                                                     static_cast<float*>(x_perm), R, H);
   return hipGetLastError();
 }
 

@@ -180,6 +180,17 @@ int moe_expert_ffn_bwd_data(const moe_dims* d, const void* dy, const void* dout,
                             const void* ab, void* dab, void* dx_rows, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* The two GEMMs of moe_expert_ffn_bwd_data, callable on their own:
+ *  _act:   dh = dy_r W2_e^T, then da/db from the saved a, b -> dab [RA, 2I]
+ *          (reads dy [R,H], dout [T,H] for shared rows, ab [RA,2I]);
+ *  _input: dx_r = da W1_e^T + db W3_e^T -> dx_rows [RA, H] (reads dab). */
+int moe_expert_ffn_bwd_act(const moe_dims* d, const void* dy, const void* dout,
+                           const int32_t* offsets, const void* w2, const void* ws2,
+                           const void* ab, void* dab, void* ws, size_t ws_bytes, void* stream);
+int moe_expert_ffn_bwd_input(const moe_dims* d, const void* dab, const int32_t* offsets,
+                             const void* w1, const void* w3, const void* ws1, const void* ws3,
+                             void* dx_rows, void* ws, size_t ws_bytes, void* stream);
+
 /* Expert FFN weight-gradient part ("W"): transposed grouped GEMM summing over
  * each expert's rows in slot order (UniEP 1.1), one owner per output tile:
  *  dW1_e = X_e^T dA_e, dW3_e = X_e^T dB_e, dW2_e = H_e^T dY_e  (float32 out;
@@ -192,6 +203,17 @@ int moe_expert_ffn_bwd_weight(const moe_dims* d, const void* x_perm, const void*
                               const int32_t* offsets, float* dw1, float* dw3, float* dw2,
                               float* dws1, float* dws3, float* dws2, void* ws, size_t ws_bytes,
                               void* stream);
+
+/* The two GEMMs of moe_expert_ffn_bwd_weight, callable on their own:
+ *  _gate_up: dW1_e = X_e^T dA_e and dW3_e = X_e^T dB_e (one pass over X);
+ *  _down:    dW2_e = H_e^T dY_e. */
+int moe_expert_ffn_bwd_weight_gate_up(const moe_dims* d, const void* x_perm, const void* x,
+                                      const void* dab, const int32_t* offsets, float* dw1,
+                                      float* dw3, float* dws1, float* dws3, void* ws,
+                                      size_t ws_bytes, void* stream);
+int moe_expert_ffn_bwd_weight_down(const moe_dims* d, const void* h, const void* dy,
+                                   const void* dout, const int32_t* offsets, float* dw2,
+                                   float* dws2, void* ws, size_t ws_bytes, void* stream);
 
 /* Dispatch backward: dx[t] = sum_k dx_rows[slot[t,k]] + sum_s dx_rows[R+s*T+t]
  * (float32 accumulation in that order, one rounding).

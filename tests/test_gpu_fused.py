@@ -1,0 +1,84 @@
+"""The fused persistent kernels (Dispatch+GroupGEMM, GroupGEMM+Combine) give
+the same bits as the unfused launch sequence, whatever the number of
+persistent workers and on every rerun (the UniEP article's bit-consistency of
+the fused, overlapped execution with strictly sequential execution), and match
+the oracle like the unfused path."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from combine_moe_route_histogram_amd import layer as L
+from gpu_util import custom_config, device_inputs, host, max_rel
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [
+    (300, 256, 8, 2, 320, 0),
+    (257, 128, 5, 3, 192, 2),
+    (520, 192, 16, 4, 128, 0),
+    (64, 128, 1, 1, 128, 1),
+]
+OUTS = ("x_perm", "ab", "h", "y", "out")
+
+
+def _run(cfg, inp, fused, workers=None):
+    if workers is None:
+        os.environ.pop("MOE_FUSED_WORKERS", None)
+    else:
+        os.environ["MOE_FUSED_WORKERS"] = str(workers)
+    try:
+        d = L.make_dims(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.n_shared, cfg.dtype)
+        b = L.Buffers(d, backward=False)
+        for t in (b.x_perm, b.ab, b.h, b.y, b.out):
+            t.fill_(7)                       # stale values must be overwritten
+        L.forward(b, device_inputs(inp), fused=fused)
+        torch.cuda.synchronize()
+        return b
+    finally:
+        os.environ.pop("MOE_FUSED_WORKERS", None)
+
+
+def _inputs(shape, dtype, seed=0):
+    T, H, E, K, I, Ns = shape
+    cfg = custom_config(T, H, E, K, I, Ns, dtype, number=200 + seed)
+    inp = synth.make_inputs(cfg, with_grad=False)
+    if E == 16:
+        inp["logits"][:, [2, 9]] = -30.0
+        inp["logits"][: T // 2, 4] += 8.0
+    return cfg, inp
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
+def test_fused_equals_unfused_bitwise(shape, dtype):
+    cfg, inp = _inputs(shape, dtype)
+    print(f"case fused shape={shape} dtype={dtype}", flush=True)
+    ref = _run(cfg, inp, fused=False)
+    got = _run(cfg, inp, fused=True)
+    for n in OUTS:
+        assert torch.equal(getattr(ref, n), getattr(got, n)), n
+    fwd = O.forward(inp, cfg.K, dtype)
+    if dtype == "bf16":
+        assert max_rel(host(got.out), fwd["out"], dtype) <= 2e-2
+
+
+@pytest.mark.parametrize("workers", [1, 7, 64])
+def test_fused_result_independent_of_worker_count(workers):
+    cfg, inp = _inputs(SHAPES[1], "bf16", seed=1)
+    print(f"case fused workers={workers}", flush=True)
+    ref = _run(cfg, inp, fused=True)
+    got = _run(cfg, inp, fused=True, workers=workers)
+    for n in OUTS:
+        assert torch.equal(getattr(ref, n), getattr(got, n)), n
+
+
+def test_fused_reruns_bit_identical():
+    cfg, inp = _inputs(SHAPES[2], "bf16", seed=2)
+    outs = [_run(cfg, inp, fused=True) for _ in range(3)]
+    for b in outs[1:]:
+        for n in OUTS:
+            assert torch.equal(getattr(outs[0], n), getattr(b, n)), n

@@ -361,14 +361,16 @@ def test_token_and_column_subsets_agree_with_full_pipeline(dtype):
 
 
 def test_synth_is_seeded_and_shaped():
-    cfg = synth.config("dsv3")
-    a = synth.make_inputs(cfg, T=64)
-    b = synth.make_inputs(cfg, T=64)
+    cfg = synth.Config("small", 77, 64, 256, 8, 3, 128, 2, 128, "bf16", "fwd+bwd", "gauss")
+    a = synth.make_inputs(cfg)
+    b = synth.make_inputs(cfg)
     for k in a:
         assert np.array_equal(a[k], b[k])
-    assert a["x"].dtype == np.uint16 and a["x"].shape == (64, 2048)
-    assert a["ws1"].shape == (2, 2048, 1408) and a["dout"].shape == (64, 2048)
-    z = synth.make_inputs(synth.config("skewed"), T=4096)
-    idx = O.route_select(z["logits"], 6)
+    assert a["x"].dtype == np.uint16 and a["x"].shape == (64, 256)
+    assert a["ws1"].shape == (2, 256, 128) and a["dout"].shape == (64, 256)
+    assert a["w2"].shape == (8, 128, 256) and a["logits"].dtype == np.float32
+    # Zipf(1.2) recipe of the skewed workload: 8 experts never picked, a heavy head
+    z = synth._zipf_logits(np.random.SeedSequence(5), 4096, 64)
+    idx = O.route_select(z, 6)
     counts = np.bincount(idx.ravel(), minlength=64)
     assert (counts == 0).sum() == 8 and counts.max() > 4 * counts[counts > 0].mean()
