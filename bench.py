@@ -1,7 +1,7 @@
 """Throughput of the MoE expert layer (forward + backward) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
-                    [--fused] [--no-cpu-baseline] [--cpu-tokens N]
+                    [--unfused] [--no-cpu-baseline] [--cpu-tokens N]
 
 One step = one pass of the whole layer over one batch of synthetic, seeded
 inputs already resident in HBM: route (top-k, histogram, slot map) ->
@@ -40,8 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral")
-    ap.add_argument("--fused", action="store_true",
-                    help="time the fused Dispatch+GEMM and GEMM+Combine entry points")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the unfused forward calls instead of the fused persistent kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=384)
     ap.add_argument("--fwd-only", action="store_true")
@@ -97,7 +97,7 @@ def main():
     d = L.make_dims(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.n_shared, cfg.dtype)
     b = L.Buffers(d, backward=backward)
     stream = torch.cuda.current_stream()
-    fused = args.fused
+    fused = not args.unfused
 
     calls = []  # (name, start_event, end_event)
 
