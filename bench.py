@@ -43,9 +43,23 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="time the unfused forward calls instead of the fused persistent kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=384)
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--fwd-only", action="store_true")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="only run a plain 256 MiB device copy three times (the reference that "
+                         "calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def copy_reference():
+    import torch
+    n = 256 * 1024 * 1024
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copied {n} bytes x3", flush=True)
 
 
 def algorithmic_work(d, b):
@@ -73,6 +87,9 @@ def algorithmic_work(d, b):
 
 def main():
     args = parse()
+    if args.copy_reference:
+        copy_reference()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the layer would shard by expert across GPUs, which is not built here)",
