@@ -51,8 +51,7 @@ __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
                                                                   const int32_t* __restrict__ slot_src,
                                                                   FusedWs w, int nt_count) {
   using C = UpCfg;
-  __shared__ __align__(16) uint8_t st0[C::STAGE_BYTES];
-  __shared__ __align__(16) uint8_t st1[C::STAGE_BYTES];
+  MOE_LDS_RING(C, ring);
   __shared__ int task_slot;
   const int n_mt = *w.n_mtiles;
   const int total = n_mt + n_mt * nt_count;
@@ -83,7 +82,7 @@ __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
           __builtin_amdgcn_s_sleep(2);
       __syncthreads();
       const TileDesc<uint16_t> d = decode_tile<uint16_t, kUp, C::BM, C::BN>(g, tm, tn);
-      run_tile_bf16<C>(g, d, st0, st1);
+      run_tile_bf16<C>(g, d, ring);
     }
   }
 }
@@ -111,8 +110,7 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
                                                                    const float* __restrict__ topk_w,
                                                                    FusedWs w, int nt_count) {
   using C = DownCfg;
-  __shared__ __align__(16) uint8_t st0[C::STAGE_BYTES];
-  __shared__ __align__(16) uint8_t st1[C::STAGE_BYTES];
+  MOE_LDS_RING(C, ring);
   __shared__ int task_slot;
   const int n_mt = *w.n_mtiles;
   const int n_gemm = n_mt * nt_count;
@@ -126,7 +124,7 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
       int tm, tn;
       band_order(task, n_mt, nt_count, tm, tn);
       const TileDesc<uint16_t> d = decode_tile<uint16_t, kDown, C::BM, C::BN>(g, tm, tn);
-      run_tile_bf16<C>(g, d, st0, st1);
+      run_tile_bf16<C>(g, d, ring);
       publish_add(&w.flags[tm]);
     } else {
       const int t0 = (task - n_gemm) * kCombineTokens;

@@ -74,15 +74,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 
 template <class C>
 __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(GemmArgs g, int mt_count, int nt_count) {
-  __shared__ __align__(16) uint8_t st0[C::STAGE_BYTES];
-  __shared__ __align__(16) uint8_t st1[C::STAGE_BYTES];
+  MOE_LDS_RING(C, ring);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   if (L >= mt_count * nt_count) return;
   int tm, tn;
   band_order(L, mt_count, nt_count, tm, tn);
   const TileDesc<uint16_t> d = decode_tile<uint16_t, C::KIND, C::BM, C::BN>(g, tm, tn);
   if (d.skip) return;
-  run_tile_bf16<C>(g, d, st0, st1);
+  run_tile_bf16<C>(g, d, ring);
 }
 
 template <int KIND>

@@ -276,7 +276,7 @@ __device__ __forceinline__ uint32_t mn_off(int k, int col, int cols) {
 // Global -> LDS copy of one operand stage.
 //  KC: rows BMN, 8 rows per 1 KiB instruction.
 //  MN: NH sub-tiles of HMN columns, 64 k rows, 1024 / (2 HMN) rows per instruction.
-template <int BMN, int NW, bool MN, int NH>
+template <int BMN, int NW, bool MN, int NH, bool RAGGED_K = false>
 struct DmaOperand {
   static constexpr int kHMN = BMN / NH;
   static constexpr int kInstr = BMN * kBK * 2 / 1024;      // 1 KiB instructions per stage
@@ -285,7 +285,7 @@ struct DmaOperand {
   static_assert(!MN || kHMN >= 128, "MN sub-tiles need >= 128 columns");
   static_assert(MN || NH == 1, "KC operands have one source");
   uint32_t off[kPerWave];   // per-lane byte offset (relative to the k slice start) or invalid
-  int krow[kPerWave];       // MN: k row of this lane (for the ragged-k check)
+  int krow[RAGGED_K ? kPerWave : 1];  // MN with ragged K: k row of this lane
   // s = row stride (KC) or k stride (MN) in elements; mn_valid per sub-tile.
   __device__ __forceinline__ void init(int64_t s, int mn_valid, int wave, int lane) {
 #pragma unroll
@@ -295,7 +295,6 @@ struct DmaOperand {
         const int r = 8 * q + (lane >> 3);
         const int c = (lane & 7) ^ ((r >> 1) & 7);
         off[i] = r < mn_valid ? (uint32_t)(r * s * 2 + c * 16) : kBufInvalid;
-        krow[i] = 0;
       } else {
         constexpr int kQHalf = kHMN * kBK * 2 / 1024;        // instructions per sub-tile
         const int qh = q % kQHalf;
@@ -304,7 +303,7 @@ struct DmaOperand {
         const int p = (byte % (2 * kHMN)) / 16;
         const int col = (p ^ (4 * (k & 3))) * 8;
         off[i] = col < mn_valid ? (uint32_t)(k * s * 2 + col * 2) : kBufInvalid;
-        krow[i] = k;
+        if constexpr (RAGGED_K) krow[i] = k;
       }
     }
   }
@@ -322,7 +321,7 @@ struct DmaOperand {
       }
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(src);
       uint32_t o = off[i];
-      if constexpr (MN) o = krow[i] < k_valid ? o : kBufInvalid;
+      if constexpr (MN && RAGGED_K) o = krow[i] < k_valid ? o : kBufInvalid;
       dma16(rs, stage + q * 1024, o);
     }
   }
@@ -377,24 +376,46 @@ __device__ __forceinline__ void b_block(int wn, int j, int& sub, int& col) {
   }
 }
 
-// The whole tile: two LDS k slices (separate LDS objects, so the compiler can
-// tell the direct loads into one from the fragment reads of the other) filled
-// alternately, MFMA over each slice with the next k step's fragments in
-// flight, then the epilogue.  The barrier at the top of each slice both waits
-// for that slice's loads and frees the other slice for the next loads, which
-// then run during the whole MFMA pass over this slice.
+template <int IMM>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt with vmcnt = IMM, expcnt and lgkmcnt left at their maximum
+  static_assert(IMM >= 0 && IMM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((IMM & 0xF) | ((IMM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that orders LDS accesses around it without making the
+// compiler drain the outstanding global->LDS loads (the ring waits for those
+// itself, slice by slice).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The LDS slices of one tile worker: separate LDS objects, so the compiler can
+// tell the loads into one slice from the fragment reads of another.
+#define MOE_LDS_RING(C, name)                                                       \
+  __shared__ __align__(16) uint8_t name##0[C::STAGE_BYTES];                         \
+  __shared__ __align__(16) uint8_t name##1[C::STAGE_BYTES];                         \
+  __shared__ __align__(16) uint8_t name##2[C::STAGES > 2 ? C::STAGE_BYTES : 16];    \
+  __shared__ __align__(16) uint8_t name##3[C::STAGES > 3 ? C::STAGE_BYTES : 16];    \
+  uint8_t* const name[4] = {name##0, name##1, name##2, name##3}
+
+// The whole tile: a ring of LDS k slices filled by direct loads, MFMA over
+// each slice with the next k step's fragments in flight, then the epilogue.
 template <class C>
-__device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d, uint8_t* st0,
-                              uint8_t* st1) {
+__device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
+                              uint8_t* const (&stages)[4]) {
   constexpr int MI = C::MI, NJ = C::NJ;
-  static_assert(C::STAGES == 2, "two LDS slices");
+  static_assert(C::STAGES >= 2 && C::STAGES <= 4, "2 to 4 LDS slices");
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / C::WGN, wn = wave % C::WGN;
 
-  DmaOperand<C::BM, C::NW, C::A_MN, 1> da;
-  DmaOperand<C::BN, C::NW, C::B_MN, C::B_NH> db;
+  // only the weight gradient has a k range (an expert's rows) that is not a
+  // whole number of slices
+  constexpr bool kRagged = KindTraits<C::KIND>::kWgrad;
+  DmaOperand<C::BM, C::NW, C::A_MN, 1, kRagged> da;
+  DmaOperand<C::BN, C::NW, C::B_MN, C::B_NH, kRagged> db;
   if constexpr (C::A_MN) da.init(d.a_sk, d.m_valid, wave, lane); else da.init(d.a_sm, d.m_valid, wave, lane);
   if constexpr (C::B_MN) db.init(d.b_sk, d.n_valid, wave, lane); else db.init(d.b_sn, d.n_valid, wave, lane);
 
@@ -446,29 +467,50 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d, ui
         bv[j] = kc_frag(tb, b_col[j] + (lane & 31), 2 * ks + (lane >> 5));
     }
   };
+  auto mfma_step = [&](const bf16x8 (&av)[MI], const bf16x8 (&bv)[NJ]) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+  };
+  // MFMAs over one slice; the fragments of k step ks+1 are read before the
+  // MFMAs of step ks are issued (scheduling fences keep that order).
   auto compute = [&](const uint8_t* st) {
     bf16x8 av[2][MI], bv[2][NJ];
     frags(st, 0, av[0], bv[0]);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       if (ks + 1 < kBK / 16) frags(st, ks + 1, av[(ks + 1) & 1], bv[(ks + 1) & 1]);
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks & 1][i], bv[ks & 1][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(av[ks & 1], bv[ks & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  if (nk > 0) issue(st0, 0);
-  for (int kt = 0; kt < nk; kt += 2) {
-    __syncthreads();                       // slice kt (st0) landed; st1 free
-    if (kt + 1 < nk) issue(st1, kt + 1);
-    compute(st0);
-    if (kt + 1 >= nk) break;
-    __syncthreads();                       // slice kt+1 (st1) landed; st0 free
-    if (kt + 2 < nk) issue(st0, kt + 2);
-    compute(st1);
+  // Ring of S slices: slice kt lives in stage kt % S.  Before computing
+  // slice kt a wave waits until at most the loads of the slices issued after
+  // it are outstanding, then a barrier makes every wave's loads of slice kt
+  // visible and frees stage (kt-1) % S, into which slice kt+S-1 is loaded
+  // while slice kt is computed.  S-1 slices of loads are in flight.
+  constexpr int S = C::STAGES;
+  constexpr int kLoads = decltype(da)::kPerWave + decltype(db)::kPerWave;
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i)
+    if (i < nk) issue(stages[i], i);
+  for (int kt0 = 0; kt0 < nk; kt0 += S) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      const int kt = kt0 + i;
+      if (kt >= nk) break;
+      const int later = min(S - 2, nk - 1 - kt);   // slices issued after kt
+      if (later >= 2) wait_vmcnt<(S >= 4 ? 2 : 0) * kLoads>();
+      else if (later == 1) wait_vmcnt<kLoads>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (kt + S - 1 < nk) issue(stages[(i + S - 1) % S], kt + S - 1);
+      compute(stages[i]);
+    }
   }
   __syncthreads();  // LDS free for the next tile of a persistent worker
 
@@ -601,22 +643,22 @@ __device__ __forceinline__ void band_order(int L, int mt_count, int nt_count, in
 // LDS k slices.  The fused kernels use the same ones, so their tiles are
 // computed exactly as by the plain launches.
 #ifndef MOE_CFG_UP
-#define MOE_CFG_UP 128, 256, 2, 2, 2
+#define MOE_CFG_UP 256, 256, 2, 4, 2
 #endif
 #ifndef MOE_CFG_DOWN
-#define MOE_CFG_DOWN 128, 256, 2, 2, 2
+#define MOE_CFG_DOWN 256, 256, 2, 4, 2
 #endif
 #ifndef MOE_CFG_BWD_UP
-#define MOE_CFG_BWD_UP 128, 256, 2, 2, 2
+#define MOE_CFG_BWD_UP 256, 256, 2, 4, 2
 #endif
 #ifndef MOE_CFG_BWD_DOWN
-#define MOE_CFG_BWD_DOWN 128, 256, 2, 2, 2
+#define MOE_CFG_BWD_DOWN 256, 256, 2, 4, 2
 #endif
 #ifndef MOE_CFG_WG_UP
-#define MOE_CFG_WG_UP 128, 256, 2, 2, 2
+#define MOE_CFG_WG_UP 256, 256, 2, 4, 2
 #endif
 #ifndef MOE_CFG_WG_DOWN
-#define MOE_CFG_WG_DOWN 128, 256, 2, 2, 2
+#define MOE_CFG_WG_DOWN 256, 256, 2, 4, 2
 #endif
 template <int KIND> struct BfPick;
 template <> struct BfPick<kUp> { using C = BfCfg<kUp, MOE_CFG_UP>; };
