@@ -36,7 +36,7 @@
 
 namespace moe {
 
-constexpr int kBK = 64;  // k per LDS stage (bf16)
+constexpr int kBK = 64;  // default k per LDS slice (bf16)
 
 template <typename S>
 struct TileDesc {
@@ -264,9 +264,13 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds_block
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t)lds_block, 16, voff, 0, 0, 0);
 }
 
-// Byte offset of (row, 16-byte chunk) inside a KC stage tile.
+// Byte offset of (row, 16-byte chunk) inside a KC slice of BK k per row.  A
+// 256-byte bank row holds 16 / (BK/8) tile rows; the chunk index is XORed with
+// the bank-row index so 16 consecutive rows' same chunk hit 16 bank groups.
+template <int BK>
 __device__ __forceinline__ uint32_t kc_off(int row, int chunk) {
-  return (uint32_t)(row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4));
+  constexpr int kCpr = BK / 8, kRpb = 16 / kCpr;
+  return (uint32_t)(row * BK * 2 + ((chunk ^ ((row / kRpb) & (kCpr - 1))) << 4));
 }
 // Byte offset of (k, column) inside an MN sub-tile of `cols` columns.
 __device__ __forceinline__ uint32_t mn_off(int k, int col, int cols) {
@@ -276,10 +280,11 @@ __device__ __forceinline__ uint32_t mn_off(int k, int col, int cols) {
 // Global -> LDS copy of one operand stage.
 //  KC: rows BMN, 8 rows per 1 KiB instruction.
 //  MN: NH sub-tiles of HMN columns, 64 k rows, 1024 / (2 HMN) rows per instruction.
-template <int BMN, int NW, bool MN, int NH, bool RAGGED_K = false>
+template <int BMN, int NW, bool MN, int NH, bool RAGGED_K, int BK>
 struct DmaOperand {
   static constexpr int kHMN = BMN / NH;
-  static constexpr int kInstr = BMN * kBK * 2 / 1024;      // 1 KiB instructions per stage
+  static constexpr int kCpr = BK / 8;                       // 16-byte chunks per KC row
+  static constexpr int kInstr = BMN * BK * 2 / 1024;        // 1 KiB instructions per slice
   static constexpr int kPerWave = kInstr / NW;
   static_assert(kInstr % NW == 0, "stage copy must split evenly over the waves");
   static_assert(!MN || kHMN >= 128, "MN sub-tiles need >= 128 columns");
@@ -292,11 +297,12 @@ struct DmaOperand {
     for (int i = 0; i < kPerWave; ++i) {
       const int q = wave + NW * i;                           // instruction index in the stage
       if constexpr (!MN) {
-        const int r = 8 * q + (lane >> 3);
-        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        constexpr int kRpi = 1024 / (BK * 2);                 // rows per instruction
+        const int r = kRpi * q + lane / kCpr;
+        const int c = (lane % kCpr) ^ ((r / (16 / kCpr)) & (kCpr - 1));
         off[i] = r < mn_valid ? (uint32_t)(r * s * 2 + c * 16) : kBufInvalid;
       } else {
-        constexpr int kQHalf = kHMN * kBK * 2 / 1024;        // instructions per sub-tile
+        constexpr int kQHalf = kHMN * BK * 2 / 1024;         // instructions per sub-tile
         const int qh = q % kQHalf;
         const int byte = qh * 1024 + 16 * lane;
         const int k = byte / (2 * kHMN);
@@ -316,7 +322,7 @@ struct DmaOperand {
       const int q = wave + NW * i;
       const uint16_t* src = src0;
       if constexpr (NH == 2) {
-        constexpr int kQHalf = kHMN * kBK * 2 / 1024;
+        constexpr int kQHalf = kHMN * BK * 2 / 1024;
         if (q >= kQHalf) src = src1;
       }
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(src);
@@ -327,16 +333,18 @@ struct DmaOperand {
   }
 };
 
-template <int KIND_, int BM_, int BN_, int WGM_, int WGN_, int STAGES_>
+template <int KIND_, int BM_, int BN_, int WGM_, int WGN_, int STAGES_, int BK_ = kBK>
 struct BfCfg {
   static constexpr int KIND = KIND_, BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, STAGES = STAGES_;
+  static constexpr int BK = BK_;
+  static_assert(BK == 32 || BK == 64, "k slice of 32 or 64");
   static constexpr int NW = WGM * WGN, NT = NW * kWave;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int MI = WM / 32, NJ = WN / 32;
   static constexpr bool PAIRED = KindTraits<KIND>::kPaired;
   static constexpr bool A_MN = KindTraits<KIND>::kAMn, B_MN = KindTraits<KIND>::kBMn;
   static constexpr int B_NH = PAIRED ? 2 : 1;
-  static constexpr int A_BYTES = BM * kBK * 2, B_BYTES = BN * kBK * 2;
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be made of 32x32 blocks");
@@ -346,8 +354,9 @@ struct BfCfg {
 };
 
 // Fragment reads.  kc_frag: 8 consecutive k (16-byte chunk ch) of row `row`.
+template <int BK>
 __device__ __forceinline__ bf16x8 kc_frag(const uint8_t* tile, int row, int ch) {
-  return *reinterpret_cast<const bf16x8*>(tile + kc_off(row, ch));
+  return *reinterpret_cast<const bf16x8*>(tile + kc_off<BK>(row, ch));
 }
 // mn_frag: for MFMA lane l, column col0 + (l % 32) and k rows 8 * (l / 32) +
 // 16 * ks .. + 8 of an MN sub-tile of `cols` columns.
@@ -399,6 +408,127 @@ __device__ __forceinline__ void lds_barrier() {
   __shared__ __align__(16) uint8_t name##3[C::STAGES > 3 ? C::STAGE_BYTES : 16];    \
   uint8_t* const name[4] = {name##0, name##1, name##2, name##3}
 
+// Epilogue of one tile.  Each wave owns a WM x WN block of the tile; it moves
+// one 32-row block row of its accumulators at a time through its own LDS
+// region (32 rows x 64 f32, row pitch 72 floats so the scattered writes of the
+// 32x32 accumulator layout and the row reads below are both free of bank
+// conflicts), then every lane handles 4 consecutive columns of one row:
+// 8-byte bf16 or 16-byte f32 stores, 8-byte loads of the saved activations.
+// Paired kinds keep the two values of an output column in region columns c and
+// c + 32 (blocks j and j + NJ/2).
+constexpr int kEpiPitch = 72;                      // floats per region row
+constexpr int kEpiRegionBytes = 32 * kEpiPitch * 4;
+
+__device__ __forceinline__ void st_bf16x4(void* p, const float* v) {
+  u32x2 w;
+  w[0] = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+  w[1] = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+  *reinterpret_cast<u32x2*>(p) = w;
+}
+__device__ __forceinline__ void ld_bf16x4(const void* p, float* v) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  v[0] = __uint_as_float(w[0] << 16); v[1] = __uint_as_float(w[0] & 0xFFFF0000u);
+  v[2] = __uint_as_float(w[1] << 16); v[3] = __uint_as_float(w[1] & 0xFFFF0000u);
+}
+__device__ __forceinline__ float fast_sigmoid(float a) { return __frcp_rn(1.0f + __expf(-a)); }
+
+template <class C>
+__device__ __forceinline__ void epilogue_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
+                                              const f32x16 (&acc)[C::MI][C::NJ],
+                                              uint8_t* const (&stages)[4], int wave, int lane) {
+  constexpr int MI = C::MI, NJ = C::NJ, KIND = C::KIND;
+  static_assert(C::WN == 64 && NJ == 2, "epilogue staging assumes 64-column wave tiles");
+  static_assert(4 * kEpiRegionBytes <= C::STAGE_BYTES, "epilogue regions fit in two slices");
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  float* reg = reinterpret_cast<float*>(((wave >> 2) ? stages[1] : stages[0]) + (wave & 3) * kEpiRegionBytes);
+  const int64_t H = g.H, I = g.I;
+  // output column of region column 0 (paired: of columns 0 and 32)
+  const int ncol0 = C::PAIRED ? wn * (C::WN / 2) : wn * C::WN;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    // accumulator block row i -> region
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        reg[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kEpiPitch + 32 * j + (lane & 31)] = acc[i][j][r];
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's own region is written
+    const int m_base = wm * C::WM + 32 * i;
+    if constexpr (C::PAIRED) {
+      // 8 lanes per row, 4 columns of both values each; 8 rows per pass
+#pragma unroll
+      for (int pass = 0; pass < 4; ++pass) {
+        const int q = pass * 8 + (lane >> 3);
+        const int c4 = 4 * (lane & 7);
+        const int m = m_base + q, n = ncol0 + c4;
+        float v[4], w[4];
+        const float4 va = *reinterpret_cast<const float4*>(reg + q * kEpiPitch + c4);
+        const float4 vb = *reinterpret_cast<const float4*>(reg + q * kEpiPitch + 32 + c4);
+        v[0] = va.x; v[1] = va.y; v[2] = va.z; v[3] = va.w;
+        w[0] = vb.x; w[1] = vb.y; w[2] = vb.z; w[3] = vb.w;
+        if (m < d.m_valid && n < d.n_valid) {
+          const int64_t row = d.row0 + m, col = d.col0 + n;
+          if constexpr (KIND == kUp) {
+            uint16_t* ab = static_cast<uint16_t*>(g.o_ab) + row * 2 * I;
+            st_bf16x4(ab + col, v);
+            st_bf16x4(ab + I + col, w);
+            float h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = v[e] * fast_sigmoid(v[e]) * w[e];
+            st_bf16x4(static_cast<uint16_t*>(g.o_h) + row * I + col, h);
+          } else {  // kWgUp: dW1 | dW3 columns of expert / shared group
+            const bool shared = d.group >= g.E;
+            const int64_t e = shared ? d.group - g.E : d.group;
+            float* w1 = (shared ? g.o_dws1 : g.o_dw1) + e * H * I + row * I + col;
+            float* w3 = (shared ? g.o_dws3 : g.o_dw3) + e * H * I + row * I + col;
+            __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(v), reinterpret_cast<f32x4*>(w1));
+            __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(w), reinterpret_cast<f32x4*>(w3));
+          }
+        }
+      }
+    } else {
+      // 16 lanes per row, 4 columns each; 4 rows per pass
+#pragma unroll
+      for (int pass = 0; pass < 8; ++pass) {
+        const int q = pass * 4 + (lane >> 4);
+        const int c4 = 4 * (lane & 15);
+        const int m = m_base + q, n = ncol0 + c4;
+        const float4 va = *reinterpret_cast<const float4*>(reg + q * kEpiPitch + c4);
+        float v[4] = {va.x, va.y, va.z, va.w};
+        if (m < d.m_valid && n < d.n_valid) {
+          const int64_t row = d.row0 + m, col = d.col0 + n;
+          if constexpr (KIND == kDown) {
+            st_bf16x4(static_cast<uint16_t*>(g.o_y) + row * H + col, v);
+          } else if constexpr (KIND == kBwdDown) {
+            st_bf16x4(static_cast<uint16_t*>(g.o_dx) + row * H + col, v);
+          } else if constexpr (KIND == kBwdUp) {
+            const uint16_t* ab = static_cast<const uint16_t*>(g.ab) + row * 2 * I;
+            float a[4], b[4], da[4], db[4];
+            ld_bf16x4(ab + col, a);
+            ld_bf16x4(ab + I + col, b);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float sg = fast_sigmoid(a[e]);
+              da[e] = v[e] * b[e] * sg * (1.0f + a[e] * (1.0f - sg));
+              db[e] = v[e] * a[e] * sg;
+            }
+            uint16_t* dab = static_cast<uint16_t*>(g.o_dab) + row * 2 * I;
+            st_bf16x4(dab + col, da);
+            st_bf16x4(dab + I + col, db);
+          } else {  // kWgDown
+            const bool shared = d.group >= g.E;
+            const int64_t e = shared ? d.group - g.E : d.group;
+            float* w2 = (shared ? g.o_dws2 : g.o_dw2) + e * I * H + row * H + col;
+            __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(v), reinterpret_cast<f32x4*>(w2));
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // region reads done before the next block row
+  }
+  __syncthreads();  // regions free for the next tile of a persistent worker
+}
+
 // The whole tile: a ring of LDS k slices filled by direct loads, MFMA over
 // each slice with the next k step's fragments in flight, then the epilogue.
 template <class C>
@@ -414,14 +544,15 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
   // only the weight gradient has a k range (an expert's rows) that is not a
   // whole number of slices
   constexpr bool kRagged = KindTraits<C::KIND>::kWgrad;
-  DmaOperand<C::BM, C::NW, C::A_MN, 1, kRagged> da;
-  DmaOperand<C::BN, C::NW, C::B_MN, C::B_NH, kRagged> db;
+  DmaOperand<C::BM, C::NW, C::A_MN, 1, kRagged, C::BK> da;
+  DmaOperand<C::BN, C::NW, C::B_MN, C::B_NH, kRagged, C::BK> db;
   if constexpr (C::A_MN) da.init(d.a_sk, d.m_valid, wave, lane); else da.init(d.a_sm, d.m_valid, wave, lane);
   if constexpr (C::B_MN) db.init(d.b_sk, d.n_valid, wave, lane); else db.init(d.b_sn, d.n_valid, wave, lane);
 
-  const int nk = (d.k_len + kBK - 1) / kBK;
+  constexpr int BK = C::BK;
+  const int nk = (d.k_len + BK - 1) / BK;
   auto issue = [&](uint8_t* st, int kt) {
-    const int k0 = kt * kBK;
+    const int k0 = kt * BK;
     if constexpr (C::A_MN)
       da.issue(st, d.a + (int64_t)k0 * d.a_sk, nullptr, d.k_len - k0, wave);
     else
@@ -457,14 +588,14 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
       if constexpr (C::A_MN)
         av[i] = mn_frag(ta, C::BM, a_row[i], ks, lane);
       else
-        av[i] = kc_frag(ta, a_row[i] + (lane & 31), 2 * ks + (lane >> 5));
+        av[i] = kc_frag<BK>(ta, a_row[i] + (lane & 31), 2 * ks + (lane >> 5));
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       if constexpr (C::B_MN)
         bv[j] = mn_frag(tb + b_sub[j] * kBSubBytes, kBCols, b_col[j], ks, lane);
       else
-        bv[j] = kc_frag(tb, b_col[j] + (lane & 31), 2 * ks + (lane >> 5));
+        bv[j] = kc_frag<BK>(tb, b_col[j] + (lane & 31), 2 * ks + (lane >> 5));
     }
   };
   auto mfma_step = [&](const bf16x8 (&av)[MI], const bf16x8 (&bv)[NJ]) {
@@ -480,8 +611,8 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
     bf16x8 av[2][MI], bv[2][NJ];
     frags(st, 0, av[0], bv[0]);
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      if (ks + 1 < kBK / 16) frags(st, ks + 1, av[(ks + 1) & 1], bv[(ks + 1) & 1]);
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) frags(st, ks + 1, av[(ks + 1) & 1], bv[(ks + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
       mfma_step(av[ks & 1], bv[ks & 1]);
       __builtin_amdgcn_sched_barrier(0);
@@ -514,36 +645,7 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
   }
   __syncthreads();  // LDS free for the next tile of a persistent worker
 
-  // Epilogue.  32x32 accumulator layout: lane holds column (lane & 31) and
-  // rows 8*(r/4) + 4*(lane/32) + (r%4), r = 0..15.
-  const int ncol = lane & 31;
-#pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    if constexpr (C::PAIRED) {
-      constexpr int HJ = NJ / 2;
-#pragma unroll
-      for (int j = 0; j < HJ; ++j) {
-        const int n = wn * (C::WN / 2) + 32 * j + ncol;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = wm * C::WM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (m < d.m_valid && n < d.n_valid)
-            emit<uint16_t, C::KIND>(g, d, m, n, acc[i][j][r], acc[i][j + HJ][r]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int n = wn * C::WN + 32 * j + ncol;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = wm * C::WM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (m < d.m_valid && n < d.n_valid)
-            emit<uint16_t, C::KIND>(g, d, m, n, acc[i][j][r], 0.f);
-        }
-      }
-    }
-  }
+  epilogue_bf16<C>(g, d, acc, stages, wave, lane);
 }
 
 // ------------------------------------------------------------------ f32 ----
