@@ -1,18 +1,26 @@
 // Fused persistent kernels: Dispatch+GroupGEMM and GroupGEMM+Combine.
 //
 // UniEP article, section 2.1/2.2: one launch per fused stage, a fixed set of
-// persistent workers, a single global atomic counter as the task cursor over
-// a linear task space -- the communication (here: gather) tasks first, the
-// GroupGEMM tiles after them -- and a scoreboard of per-tile readiness flags
-// in global memory that a compute task polls before it starts.  On one GPU the
-// "communication" of dispatch is the gather of token rows into the expert-
-// contiguous buffer, and the relay/arrival part of the scoreboard collapses to
-// one flag per GEMM row tile, set once all its rows are written.
+// persistent workers that take tasks from global atomic cursors -- the
+// communication (here: gather) tasks first, the GroupGEMM tiles after them --
+// and a scoreboard of per-tile readiness flags in global memory that a
+// compute task polls before it starts.  On one GPU the "communication" of
+// dispatch is the gather of token rows into the expert-contiguous buffer, and
+// the relay/arrival part of the scoreboard collapses to one flag per GEMM row
+// tile, set once all its rows are written.
 //
-// Deadlock freedom: a task only ever waits on tasks with smaller indices, and
-// every such task was claimed from the cursor by a worker that is running and
-// never waits itself (gather tasks, GEMM tiles of the combine kernel), so the
-// wait always ends, whatever the number of resident workers.
+// MI355X difference from the single cursor of the article: the GEMM tiles are
+// split into 8 contiguous ranges in the plain launch's tile order, one per XCD
+// (workers are handed to the XCDs round robin, worker b to XCD b % 8), each
+// with its own cursor; a worker takes tiles from its XCD's range, then steals
+// from the others.  Tiles that share weight columns and token rows then run
+// on one XCD and share its L2, as in the plain launch.
+//
+// Deadlock freedom: a waiting task only waits on tasks of an earlier phase
+// (GEMM tiles on gathers; combine rows on GEMM tiles), and a worker enters a
+// phase only once every task of the phase before it has been claimed, by a
+// worker that is running and never waits inside that phase, so every wait
+// ends, whatever the number of resident workers.
 //
 // Determinism: every GEMM tile runs the same tile code with the same operands
 // as the plain launch and every combine row the same combine code, so the
@@ -23,25 +31,51 @@
 
 namespace moe {
 
+// The claimed index is broadcast with readfirstlane so the compiler sees it
+// as uniform: every loop around a claim then has a uniform exit.  Otherwise
+// the compiler may treat the exit as divergent and restructure the loop so
+// that thread 0 (which publishes and claims) leaves it while the other lanes
+// go round again on the old index -- a livelock across the barriers.
 __device__ __forceinline__ int claim_task(int32_t* cursor, int* slot) {
   if (threadIdx.x == 0) *slot = atomicAdd(cursor, 1);
   __syncthreads();
-  const int task = *slot;
+  const int task = __builtin_amdgcn_readfirstlane(*slot);
   __syncthreads();
   return task;
 }
 
 // Every wave's global stores have reached L2, then one release publishes them.
+// The trailing barrier keeps thread 0's publish and its next claim in separate
+// convergent regions, so the compiler cannot merge them across the loop edge
+// into a thread-0-only path (which would split thread 0 off the claim loop).
 __device__ __forceinline__ void publish_set(int32_t* flag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
 }
 __device__ __forceinline__ void publish_add(int32_t* counter) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0)
     __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+}
+
+// Run every GEMM tile of the ranges, own XCD's range first: tile(L) for the
+// logical tiles L in [0, n).
+template <class F>
+__device__ __forceinline__ void for_tiles_xcd_ranges(int32_t* cursors, int n, int* slot, F&& tile) {
+  const int home = blockIdx.x % kXcds;
+  for (int q = 0; q < kXcds; ++q) {
+    const int r = (home + q) % kXcds;
+    const int lo = (int)((int64_t)n * r / kXcds), hi = (int)((int64_t)n * (r + 1) / kXcds);
+    for (;;) {
+      const int L = lo + claim_task(&cursors[r], slot);
+      if (L >= hi) break;
+      tile(L);
+    }
+  }
 }
 
 using UpCfg = BfPick<kUp>::C;
@@ -54,37 +88,36 @@ __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
   MOE_LDS_RING(C, ring);
   __shared__ int task_slot;
   const int n_mt = *w.n_mtiles;
-  const int total = n_mt + n_mt * nt_count;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int nvec = g.H / 8;
+  // phase 1: gather tasks -- x_perm rows of one row tile from their tokens
   for (;;) {
-    const int task = claim_task(w.cursor, &task_slot);
-    if (task >= total) break;
-    if (task < n_mt) {
-      // gather task: x_perm rows of one row tile from their tokens
-      const int4 mt = w.mtiles[task];
-      if (mt.x < g.E) {
-        const uint16_t* x = static_cast<const uint16_t*>(g.x);
-        uint16_t* xp = static_cast<uint16_t*>(g.o_x_perm);
-        for (int r = wave; r < mt.z; r += C::NW) {
-          const int64_t s = mt.y + r;
-          const char* src = reinterpret_cast<const char*>(x + (int64_t)slot_src[s] * g.H);
-          char* dst = reinterpret_cast<char*>(xp + s * g.H);
-          for (int v = lane; v < nvec; v += kWave) st16(dst + (int64_t)v * 16, ld16(src + (int64_t)v * 16));
-        }
+    const int task = claim_task(&w.cursor[0], &task_slot);
+    if (task >= n_mt) break;
+    const int4 mt = w.mtiles[task];
+    if (mt.x < g.E) {
+      const uint16_t* x = static_cast<const uint16_t*>(g.x);
+      uint16_t* xp = static_cast<uint16_t*>(g.o_x_perm);
+      for (int r = wave; r < mt.z; r += C::NW) {
+        const int64_t s = mt.y + r;
+        const char* src = reinterpret_cast<const char*>(x + (int64_t)slot_src[s] * g.H);
+        char* dst = reinterpret_cast<char*>(xp + s * g.H);
+        for (int v = lane; v < nvec; v += kWave) st16(dst + (int64_t)v * 16, ld16(src + (int64_t)v * 16));
       }
-      publish_set(&w.flags[task]);
-    } else {
-      int tm, tn;
-      band_order(task - n_mt, n_mt, nt_count, tm, tn);
-      if (threadIdx.x == 0)
-        while (__hip_atomic_load(&w.flags[tm], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0)
-          __builtin_amdgcn_s_sleep(2);
-      __syncthreads();
-      const TileDesc<uint16_t> d = decode_tile<uint16_t, kUp, C::BM, C::BN>(g, tm, tn);
-      run_tile_bf16<C>(g, d, ring);
     }
+    publish_set(&w.flags[task]);
   }
+  // phase 2: GEMM tiles, each once its row tile is gathered
+  for_tiles_xcd_ranges(w.cursor + 1, n_mt * nt_count, &task_slot, [&](int L) {
+    int tm, tn;
+    band_order(L, n_mt, nt_count, tm, tn);
+    if (threadIdx.x == 0)
+      while (__hip_atomic_load(&w.flags[tm], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0)
+        __builtin_amdgcn_s_sleep(2);
+    __syncthreads();
+    const TileDesc<uint16_t> d = decode_tile<uint16_t, kUp, C::BM, C::BN>(g, tm, tn);
+    run_tile_bf16<C>(g, d, ring);
+  });
 }
 
 // Row tile of all-rows index `row`: the group from the expert offsets (or the
@@ -113,36 +146,35 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
   MOE_LDS_RING(C, ring);
   __shared__ int task_slot;
   const int n_mt = *w.n_mtiles;
-  const int n_gemm = n_mt * nt_count;
   const int n_comb = (g.T + kCombineTokens - 1) / kCombineTokens;
-  const int total = n_gemm + n_comb;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  // phase 1: GEMM tiles; each completed tile counts towards its row tile
+  for_tiles_xcd_ranges(w.cursor + 1, n_mt * nt_count, &task_slot, [&](int L) {
+    int tm, tn;
+    band_order(L, n_mt, nt_count, tm, tn);
+    const TileDesc<uint16_t> d = decode_tile<uint16_t, kDown, C::BM, C::BN>(g, tm, tn);
+    run_tile_bf16<C>(g, d, ring);
+    publish_add(&w.flags[tm]);
+  });
+  // phase 2: combine tasks, each token once all its rows' tiles are done
   for (;;) {
-    const int task = claim_task(w.cursor, &task_slot);
-    if (task >= total) break;
-    if (task < n_gemm) {
-      int tm, tn;
-      band_order(task, n_mt, nt_count, tm, tn);
-      const TileDesc<uint16_t> d = decode_tile<uint16_t, kDown, C::BM, C::BN>(g, tm, tn);
-      run_tile_bf16<C>(g, d, ring);
-      publish_add(&w.flags[tm]);
-    } else {
-      const int t0 = (task - n_gemm) * kCombineTokens;
-      const int t1 = min(g.T, t0 + kCombineTokens);
-      for (int t = t0 + wave; t < t1; t += C::NW) {
-        // the row tiles holding the token's routed rows (q < K) and its
-        // shared-expert rows (q >= K) must all be complete
-        for (int q = lane; q < g.K + g.Ns; q += kWave) {
-          const int64_t row = q < g.K ? (int64_t)slot[(int64_t)t * g.K + q]
-                                      : g.R + (int64_t)(q - g.K) * g.T + t;
-          const int tile = tile_of_row(row, g, w.first_tile, C::BM);
-          while (__hip_atomic_load(&w.flags[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nt_count)
-            __builtin_amdgcn_s_sleep(2);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        combine_row<uint16_t>(static_cast<const uint16_t*>(g.o_y), slot, topk_w,
-                              static_cast<uint16_t*>(g.o_out), t, g.T, g.H, g.K, g.Ns, lane);
+    const int task = claim_task(&w.cursor[0], &task_slot);
+    if (task >= n_comb) break;
+    const int t0 = task * kCombineTokens;
+    const int t1 = min(g.T, t0 + kCombineTokens);
+    for (int t = t0 + wave; t < t1; t += C::NW) {
+      // the row tiles holding the token's routed rows (q < K) and its
+      // shared-expert rows (q >= K) must all be complete
+      for (int q = lane; q < g.K + g.Ns; q += kWave) {
+        const int64_t row = q < g.K ? (int64_t)slot[(int64_t)t * g.K + q]
+                                    : g.R + (int64_t)(q - g.K) * g.T + t;
+        const int tile = tile_of_row(row, g, w.first_tile, C::BM);
+        while (__hip_atomic_load(&w.flags[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nt_count)
+          __builtin_amdgcn_s_sleep(2);
       }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      combine_row<uint16_t>(static_cast<const uint16_t*>(g.o_y), slot, topk_w,
+                            static_cast<uint16_t*>(g.o_out), t, g.T, g.H, g.K, g.Ns, lane);
     }
   }
 }
@@ -153,7 +185,7 @@ hipError_t launch_dispatch_ffn(const GemmArgs& a0, const int32_t* slot_src, cons
   a.mtiles = w.mtiles;
   a.n_mtiles = w.n_mtiles;
   hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, UpCfg::BM, w.mtiles, w.n_mtiles,
-                             w.first_tile, w.flags, w.mt_bound + 1, st);
+                             w.first_tile, w.flags, w.mt_bound + kFusedCursors, st);
   if (e != hipSuccess) return e;
   const int nt = gemm_ntiles<kUp>(a.H, a.I, UpCfg::BN);
   dispatch_ffn_kernel<<<w.workers, UpCfg::NT, 0, st>>>(a, slot_src, w, nt);
@@ -166,7 +198,7 @@ hipError_t launch_ffn_combine(const GemmArgs& a0, const int32_t* slot, const flo
   a.mtiles = w.mtiles;
   a.n_mtiles = w.n_mtiles;
   hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, DownCfg::BM, w.mtiles, w.n_mtiles,
-                             w.first_tile, w.flags, w.mt_bound + 1, st);
+                             w.first_tile, w.flags, w.mt_bound + kFusedCursors, st);
   if (e != hipSuccess) return e;
   const int nt = gemm_ntiles<kDown>(a.H, a.I, DownCfg::BN);
   ffn_combine_kernel<<<w.workers, DownCfg::NT, 0, st>>>(a, slot, topk_w, w, nt);

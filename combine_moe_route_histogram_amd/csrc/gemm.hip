@@ -73,7 +73,8 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 }
 
 template <class C>
-__global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(GemmArgs g, int mt_count, int nt_count) {
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
+void gemm_bf16_kernel(GemmArgs g, int mt_count, int nt_count) {
   MOE_LDS_RING(C, ring);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   if (L >= mt_count * nt_count) return;

@@ -314,9 +314,10 @@ struct DmaOperand {
     }
   }
   // Issue the copy of one k slice.  src0/src1: operand at (k slice start,
-  // column 0) of sub-tile 0/1 (KC: row 0 at k0); k_valid: valid k rows (MN).
+  // column 0) of sub-tile 0/1 (KC: row 0 at k0); k_valid: valid k rows (MN);
+  // live false: the slice lies past the end of k and is filled with zeros.
   __device__ __forceinline__ void issue(uint8_t* stage, const uint16_t* src0, const uint16_t* src1,
-                                        int k_valid, int wave) const {
+                                        int k_valid, bool live, int wave) const {
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int q = wave + NW * i;
@@ -326,7 +327,7 @@ struct DmaOperand {
         if (q >= kQHalf) src = src1;
       }
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(src);
-      uint32_t o = off[i];
+      uint32_t o = live ? off[i] : kBufInvalid;
       if constexpr (MN && RAGGED_K) o = krow[i] < k_valid ? o : kBufInvalid;
       dma16(rs, stage + q * 1024, o);
     }
@@ -385,6 +386,33 @@ __device__ __forceinline__ void b_block(int wn, int j, int& sub, int& col) {
   }
 }
 
+// Scheduling pattern for one k step: NM MFMAs, each followed by its share of
+// the ND LDS fragment reads and the NV global->LDS loads, so the matrix pipe
+// is fed while reads and loads issue instead of waiting behind a burst of them.
+template <int T, int NM, int ND, int NV>
+__device__ __forceinline__ void interleave_step() {
+  if constexpr (T < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    constexpr int nd = ND * (T + 1) / NM - ND * T / NM;
+    constexpr int nv = NV * (T + 1) / NM - NV * T / NM;
+    if constexpr (nd > 0) __builtin_amdgcn_sched_group_barrier(0x100, nd, 0);   // LDS reads
+    if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x020, nv, 0);   // VMEM loads
+    interleave_step<T + 1, NM, ND, NV>();
+  }
+}
+
+// f(std::integral_constant<int, n>) for a run-time n in [0, N].
+template <int N, class F>
+__device__ __forceinline__ void with_count(int n, F&& f) {
+  if constexpr (N >= 0) {
+    if (n == N) {
+      f(std::integral_constant<int, N>{});
+      return;
+    }
+    with_count<N - 1>(n, f);
+  }
+}
+
 template <int IMM>
 __device__ __forceinline__ void wait_vmcnt() {
   // s_waitcnt with vmcnt = IMM, expcnt and lgkmcnt left at their maximum
@@ -396,7 +424,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // compiler drain the outstanding global->LDS loads (the ring waits for those
 // itself, slice by slice).
 __device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), visible to the compiler's wait tracking
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // The LDS slices of one tile worker: separate LDS objects, so the compiler can
@@ -409,9 +438,9 @@ __device__ __forceinline__ void lds_barrier() {
   uint8_t* const name[4] = {name##0, name##1, name##2, name##3}
 
 // Epilogue of one tile.  Each wave owns a WM x WN block of the tile; it moves
-// one 32-row block row of its accumulators at a time through its own LDS
-// region (32 rows x 64 f32, row pitch 72 floats so the scattered writes of the
-// 32x32 accumulator layout and the row reads below are both free of bank
+// its accumulators, 32 rows x 64 columns (two 32x32 blocks) at a time, through
+// its own LDS region (row pitch 72 floats so the scattered writes of the 32x32
+// accumulator layout and the row reads below are both free of bank
 // conflicts), then every lane handles 4 consecutive columns of one row:
 // 8-byte bf16 or 16-byte f32 stores, 8-byte loads of the saved activations.
 // Paired kinds keep the two values of an output column in region columns c and
@@ -437,94 +466,105 @@ __device__ __forceinline__ void epilogue_bf16(const GemmArgs& g, const TileDesc<
                                               const f32x16 (&acc)[C::MI][C::NJ],
                                               uint8_t* const (&stages)[4], int wave, int lane) {
   constexpr int MI = C::MI, NJ = C::NJ, KIND = C::KIND;
-  static_assert(C::WN == 64 && NJ == 2, "epilogue staging assumes 64-column wave tiles");
-  static_assert(4 * kEpiRegionBytes <= C::STAGE_BYTES, "epilogue regions fit in two slices");
+  static_assert(NJ % 2 == 0, "the region takes two 32-column blocks at a time");
+  constexpr int kRps = C::STAGE_BYTES / kEpiRegionBytes;   // regions per LDS slice
+  static_assert(kRps >= 1 && (C::NW + kRps - 1) / kRps <= C::STAGES, "epilogue regions fit in the slices");
   const int wm = wave / C::WGN, wn = wave % C::WGN;
-  float* reg = reinterpret_cast<float*>(((wave >> 2) ? stages[1] : stages[0]) + (wave & 3) * kEpiRegionBytes);
+  const int rs = wave / kRps;
+  uint8_t* const rbase = rs == 0 ? stages[0] : rs == 1 ? stages[1] : rs == 2 ? stages[2] : stages[3];
+  float* reg = reinterpret_cast<float*>(rbase + (wave - rs * kRps) * kEpiRegionBytes);
   const int64_t H = g.H, I = g.I;
-  // output column of region column 0 (paired: of columns 0 and 32)
+  // output column of the wave's first column (paired: of both values)
   const int ncol0 = C::PAIRED ? wn * (C::WN / 2) : wn * C::WN;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
-    // accumulator block row i -> region
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int hc = 0; hc < NJ / 2; ++hc) {
+      // two accumulator blocks -> region columns 0..31 and 32..63: paired
+      // kinds take block hc and its partner hc + NJ/2 (same output columns),
+      // others two neighbouring blocks
+      const int j0 = C::PAIRED ? hc : 2 * hc;
+      const int j1 = C::PAIRED ? hc + NJ / 2 : 2 * hc + 1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        reg[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kEpiPitch + 32 * j + (lane & 31)] = acc[i][j][r];
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's own region is written
-    const int m_base = wm * C::WM + 32 * i;
-    if constexpr (C::PAIRED) {
-      // 8 lanes per row, 4 columns of both values each; 8 rows per pass
-#pragma unroll
-      for (int pass = 0; pass < 4; ++pass) {
-        const int q = pass * 8 + (lane >> 3);
-        const int c4 = 4 * (lane & 7);
-        const int m = m_base + q, n = ncol0 + c4;
-        float v[4], w[4];
-        const float4 va = *reinterpret_cast<const float4*>(reg + q * kEpiPitch + c4);
-        const float4 vb = *reinterpret_cast<const float4*>(reg + q * kEpiPitch + 32 + c4);
-        v[0] = va.x; v[1] = va.y; v[2] = va.z; v[3] = va.w;
-        w[0] = vb.x; w[1] = vb.y; w[2] = vb.z; w[3] = vb.w;
-        if (m < d.m_valid && n < d.n_valid) {
-          const int64_t row = d.row0 + m, col = d.col0 + n;
-          if constexpr (KIND == kUp) {
-            uint16_t* ab = static_cast<uint16_t*>(g.o_ab) + row * 2 * I;
-            st_bf16x4(ab + col, v);
-            st_bf16x4(ab + I + col, w);
-            float h[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) h[e] = v[e] * fast_sigmoid(v[e]) * w[e];
-            st_bf16x4(static_cast<uint16_t*>(g.o_h) + row * I + col, h);
-          } else {  // kWgUp: dW1 | dW3 columns of expert / shared group
-            const bool shared = d.group >= g.E;
-            const int64_t e = shared ? d.group - g.E : d.group;
-            float* w1 = (shared ? g.o_dws1 : g.o_dw1) + e * H * I + row * I + col;
-            float* w3 = (shared ? g.o_dws3 : g.o_dw3) + e * H * I + row * I + col;
-            __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(v), reinterpret_cast<f32x4*>(w1));
-            __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(w), reinterpret_cast<f32x4*>(w3));
-          }
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        reg[row * kEpiPitch + (lane & 31)] = acc[i][j0][r];
+        reg[row * kEpiPitch + 32 + (lane & 31)] = acc[i][j1][r];
       }
-    } else {
-      // 16 lanes per row, 4 columns each; 4 rows per pass
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's own region is written
+      const int m_base = wm * C::WM + 32 * i;
+      if constexpr (C::PAIRED) {
+        // 8 lanes per row, 4 columns of both values each; 8 rows per pass
 #pragma unroll
-      for (int pass = 0; pass < 8; ++pass) {
-        const int q = pass * 4 + (lane >> 4);
-        const int c4 = 4 * (lane & 15);
-        const int m = m_base + q, n = ncol0 + c4;
-        const float4 va = *reinterpret_cast<const float4*>(reg + q * kEpiPitch + c4);
-        float v[4] = {va.x, va.y, va.z, va.w};
-        if (m < d.m_valid && n < d.n_valid) {
-          const int64_t row = d.row0 + m, col = d.col0 + n;
-          if constexpr (KIND == kDown) {
-            st_bf16x4(static_cast<uint16_t*>(g.o_y) + row * H + col, v);
-          } else if constexpr (KIND == kBwdDown) {
-            st_bf16x4(static_cast<uint16_t*>(g.o_dx) + row * H + col, v);
-          } else if constexpr (KIND == kBwdUp) {
-            const uint16_t* ab = static_cast<const uint16_t*>(g.ab) + row * 2 * I;
-            float a[4], b[4], da[4], db[4];
-            ld_bf16x4(ab + col, a);
-            ld_bf16x4(ab + I + col, b);
+        for (int pass = 0; pass < 4; ++pass) {
+          const int q = pass * 8 + (lane >> 3);
+          const int c4 = 4 * (lane & 7);
+          const int m = m_base + q, n = ncol0 + 32 * hc + c4;
+          float v[4], w[4];
+          const float4 va = *reinterpret_cast<const float4*>(reg + q * kEpiPitch + c4);
+          const float4 vb = *reinterpret_cast<const float4*>(reg + q * kEpiPitch + 32 + c4);
+          v[0] = va.x; v[1] = va.y; v[2] = va.z; v[3] = va.w;
+          w[0] = vb.x; w[1] = vb.y; w[2] = vb.z; w[3] = vb.w;
+          if (m < d.m_valid && n < d.n_valid) {
+            const int64_t row = d.row0 + m, col = d.col0 + n;
+            if constexpr (KIND == kUp) {
+              uint16_t* ab = static_cast<uint16_t*>(g.o_ab) + row * 2 * I;
+              st_bf16x4(ab + col, v);
+              st_bf16x4(ab + I + col, w);
+              float h[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float sg = fast_sigmoid(a[e]);
-              da[e] = v[e] * b[e] * sg * (1.0f + a[e] * (1.0f - sg));
-              db[e] = v[e] * a[e] * sg;
+              for (int e = 0; e < 4; ++e) h[e] = v[e] * fast_sigmoid(v[e]) * w[e];
+              st_bf16x4(static_cast<uint16_t*>(g.o_h) + row * I + col, h);
+            } else {  // kWgUp: dW1 | dW3 columns of expert / shared group
+              const bool shared = d.group >= g.E;
+              const int64_t e = shared ? d.group - g.E : d.group;
+              float* w1 = (shared ? g.o_dws1 : g.o_dw1) + e * H * I + row * I + col;
+              float* w3 = (shared ? g.o_dws3 : g.o_dw3) + e * H * I + row * I + col;
+              __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(v), reinterpret_cast<f32x4*>(w1));
+              __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(w), reinterpret_cast<f32x4*>(w3));
             }
-            uint16_t* dab = static_cast<uint16_t*>(g.o_dab) + row * 2 * I;
-            st_bf16x4(dab + col, da);
-            st_bf16x4(dab + I + col, db);
-          } else {  // kWgDown
-            const bool shared = d.group >= g.E;
-            const int64_t e = shared ? d.group - g.E : d.group;
-            float* w2 = (shared ? g.o_dws2 : g.o_dw2) + e * I * H + row * H + col;
-            __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(v), reinterpret_cast<f32x4*>(w2));
+          }
+        }
+      } else {
+        // 16 lanes per row, 4 columns each; 4 rows per pass
+#pragma unroll
+        for (int pass = 0; pass < 8; ++pass) {
+          const int q = pass * 4 + (lane >> 4);
+          const int c4 = 4 * (lane & 15);
+          const int m = m_base + q, n = ncol0 + 64 * hc + c4;
+          const float4 va = *reinterpret_cast<const float4*>(reg + q * kEpiPitch + c4);
+          float v[4] = {va.x, va.y, va.z, va.w};
+          if (m < d.m_valid && n < d.n_valid) {
+            const int64_t row = d.row0 + m, col = d.col0 + n;
+            if constexpr (KIND == kDown) {
+              st_bf16x4(static_cast<uint16_t*>(g.o_y) + row * H + col, v);
+            } else if constexpr (KIND == kBwdDown) {
+              st_bf16x4(static_cast<uint16_t*>(g.o_dx) + row * H + col, v);
+            } else if constexpr (KIND == kBwdUp) {
+              const uint16_t* ab = static_cast<const uint16_t*>(g.ab) + row * 2 * I;
+              float a[4], b[4], da[4], db[4];
+              ld_bf16x4(ab + col, a);
+              ld_bf16x4(ab + I + col, b);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float sg = fast_sigmoid(a[e]);
+                da[e] = v[e] * b[e] * sg * (1.0f + a[e] * (1.0f - sg));
+                db[e] = v[e] * a[e] * sg;
+              }
+              uint16_t* dab = static_cast<uint16_t*>(g.o_dab) + row * 2 * I;
+              st_bf16x4(dab + col, da);
+              st_bf16x4(dab + I + col, db);
+            } else {  // kWgDown
+              const bool shared = d.group >= g.E;
+              const int64_t e = shared ? d.group - g.E : d.group;
+              float* w2 = (shared ? g.o_dws2 : g.o_dw2) + e * I * H + row * H + col;
+              __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(v), reinterpret_cast<f32x4*>(w2));
+            }
           }
         }
       }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // region reads done before it is rewritten
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // region reads done before the next block row
   }
   __syncthreads();  // regions free for the next tile of a persistent worker
 }
@@ -553,15 +593,17 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
   const int nk = (d.k_len + BK - 1) / BK;
   auto issue = [&](uint8_t* st, int kt) {
     const int k0 = kt * BK;
+    const bool live = kt < nk;   // kt < nk_pad always; zero-filled past nk
     if constexpr (C::A_MN)
-      da.issue(st, d.a + (int64_t)k0 * d.a_sk, nullptr, d.k_len - k0, wave);
+      da.issue(st, d.a + (int64_t)k0 * d.a_sk, nullptr, d.k_len - k0, live, wave);
     else
-      da.issue(st, d.a + k0, nullptr, 0, wave);
+      da.issue(st, d.a + k0, nullptr, 0, live, wave);
     if constexpr (C::B_MN)
       db.issue(st + C::A_BYTES, d.b0 + (int64_t)k0 * d.b_sk,
-               C::PAIRED ? d.b1 + (int64_t)k0 * d.b_sk : nullptr, d.k_len - k0, wave);
+               C::PAIRED ? d.b1 + (int64_t)k0 * d.b_sk : nullptr, d.k_len - k0, live, wave);
     else
-      db.issue(st + C::A_BYTES, k0 < d.ksplit ? d.b0 + k0 : d.b1 + (k0 - d.ksplit), nullptr, 0, wave);
+      db.issue(st + C::A_BYTES, k0 < d.ksplit ? d.b0 + k0 : d.b1 + (k0 - d.ksplit), nullptr, 0, live,
+               wave);
   };
 
   f32x16 acc[MI][NJ];
@@ -580,69 +622,108 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
   constexpr int kBSubBytes = C::B_BYTES / C::B_NH;
   constexpr int kBCols = C::BN / C::B_NH;
 
-  auto frags = [&](const uint8_t* st, int ks, bf16x8 (&av)[MI], bf16x8 (&bv)[NJ]) {
-    const uint8_t* ta = st;
-    const uint8_t* tb = st + C::A_BYTES;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      if constexpr (C::A_MN)
-        av[i] = mn_frag(ta, C::BM, a_row[i], ks, lane);
-      else
-        av[i] = kc_frag<BK>(ta, a_row[i] + (lane & 31), 2 * ks + (lane >> 5));
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      if constexpr (C::B_MN)
-        bv[j] = mn_frag(tb + b_sub[j] * kBSubBytes, kBCols, b_col[j], ks, lane);
-      else
-        bv[j] = kc_frag<BK>(tb, b_col[j] + (lane & 31), 2 * ks + (lane >> 5));
-    }
-  };
-  auto mfma_step = [&](const bf16x8 (&av)[MI], const bf16x8 (&bv)[NJ]) {
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-  };
-  // MFMAs over one slice; the fragments of k step ks+1 are read before the
-  // MFMAs of step ks are issued (scheduling fences keep that order).
-  auto compute = [&](const uint8_t* st) {
-    bf16x8 av[2][MI], bv[2][NJ];
-    frags(st, 0, av[0], bv[0]);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks + 1 < BK / 16) frags(st, ks + 1, av[(ks + 1) & 1], bv[(ks + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_step(av[ks & 1], bv[ks & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // Ring of S slices: slice kt lives in stage kt % S.  Before computing
-  // slice kt a wave waits until at most the loads of the slices issued after
-  // it are outstanding, then a barrier makes every wave's loads of slice kt
-  // visible and frees stage (kt-1) % S, into which slice kt+S-1 is loaded
-  // while slice kt is computed.  S-1 slices of loads are in flight.
+  // Ring of S slices: slice kt lives in stage kt % S; the loads of S-1
+  // slices are in flight.  Fragments run one k step ahead of the MFMAs: step
+  // ks's fragments are read while the MFMAs of the step before it are issued,
+  // one MFMA, then a share of the reads and loads, and so on (scheduling
+  // groups keep that order); the step before slice kt's first one is the
+  // previous slice's last, whose fragments were read before the barrier that
+  // opened slice kt.  So each slice starts, right after its barrier, with the
+  // refill of the stage the previous slice freed, its first fragment reads
+  // and MFMAs that need no wait; a barrier closes the slice once this wave's
+  // loads of the next slice are in.  Nothing is in flight in LDS across the
+  // loop edge.  The slice count is padded to a multiple of S with zero-filled
+  // slices (they add exact zeros), so the loop has a single exit and the
+  // accumulators stay in place across it.
+  //
+  // NA = the wave's 32-row blocks that hold valid rows (the last row tile of
+  // an expert is partial): blocks past it issue neither fragment reads nor
+  // MFMAs, which leaves the matrix pipe to the other wave of the SIMD.  The
+  // wave still does its share of the copies and barriers.  Results of the
+  // valid rows do not depend on NA.
   constexpr int S = C::STAGES;
+  constexpr int KS = BK / 16;
+  static_assert(KS % 2 == 0, "fragment buffers alternate by k step");
   constexpr int kLoads = decltype(da)::kPerWave + decltype(db)::kPerWave;
+  const int nk_pad = (nk + S - 1) / S * S;
+  auto wait_slices = [&](int pending) {   // at most `pending` later slices outstanding
+    if (S >= 4 && pending >= 2) wait_vmcnt<(S >= 4 ? 2 : 0) * kLoads>();
+    else if (S >= 3 && pending >= 1) wait_vmcnt<(S >= 3 ? 1 : 0) * kLoads>();
+    else wait_vmcnt<0>();
+  };
 #pragma unroll
-  for (int i = 0; i < S - 1; ++i)
-    if (i < nk) issue(stages[i], i);
-  for (int kt0 = 0; kt0 < nk; kt0 += S) {
+  for (int i = 0; i < S - 1; ++i) issue(stages[i], i);
+
+  auto ring = [&](auto na_c) {
+    constexpr int NA = decltype(na_c)::value;
+    constexpr int kReads = NA == 0 ? 0 : NA * (C::A_MN ? 2 : 1) + NJ * (C::B_MN ? 2 : 1);
+    // Reads in the order the MFMAs of a step (i outer, j inner) first need
+    // them: B block 0, A block 0, the other B blocks, the other A blocks.
+    auto frags = [&](const uint8_t* st, int ks, bf16x8 (&av)[MI], bf16x8 (&bv)[NJ]) {
+      if constexpr (NA > 0) {
+        const uint8_t* ta = st;
+        const uint8_t* tb = st + C::A_BYTES;
+        auto fa = [&](int i) {
+          if constexpr (C::A_MN)
+            av[i] = mn_frag(ta, C::BM, a_row[i], ks, lane);
+          else
+            av[i] = kc_frag<BK>(ta, a_row[i] + (lane & 31), 2 * ks + (lane >> 5));
+        };
+        auto fb = [&](int j) {
+          if constexpr (C::B_MN)
+            bv[j] = mn_frag(tb + b_sub[j] * kBSubBytes, kBCols, b_col[j], ks, lane);
+          else
+            bv[j] = kc_frag<BK>(tb, b_col[j] + (lane & 31), 2 * ks + (lane >> 5));
+        };
+        fb(0);
+        fa(0);
 #pragma unroll
-    for (int i = 0; i < S; ++i) {
-      const int kt = kt0 + i;
-      if (kt >= nk) break;
-      const int later = min(S - 2, nk - 1 - kt);   // slices issued after kt
-      if (later >= 2) wait_vmcnt<(S >= 4 ? 2 : 0) * kLoads>();
-      else if (later == 1) wait_vmcnt<kLoads>();
-      else wait_vmcnt<0>();
-      lds_barrier();
-      if (kt + S - 1 < nk) issue(stages[(i + S - 1) % S], kt + S - 1);
-      compute(stages[i]);
+        for (int j = 1; j < NJ; ++j) fb(j);
+#pragma unroll
+        for (int i = 1; i < NA; ++i) fa(i);
+      }
+    };
+    auto mfma_step = [&](const bf16x8 (&av)[MI], const bf16x8 (&bv)[NJ]) {
+#pragma unroll
+      for (int i = 0; i < NA; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    };
+    bf16x8 av[2][MI], bv[2][NJ];
+    const bf16x8 zero = {};
+#pragma unroll
+    for (int i = 0; i < MI; ++i) av[1][i] = zero;   // "previous step" of slice 0: adds zeros
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bv[1][j] = zero;
+    wait_slices(S - 2);
+    lds_barrier();
+    for (int kt0 = 0; kt0 < nk_pad; kt0 += S) {
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        const int kt = kt0 + i;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          frags(stages[i], ks, av[ks & 1], bv[ks & 1]);
+          // slices past the end are zero-filled; the last wait of the loop
+          // drains them before the epilogue reuses the stages
+          if (ks == 0) issue(stages[(i + S - 1) % S], kt + S - 1);
+          mfma_step(av[(ks + 1) & 1], bv[(ks + 1) & 1]);
+          if (ks == 0)
+            interleave_step<0, NA * NJ, kReads, kLoads>();
+          else
+            interleave_step<0, NA * NJ, kReads, 0>();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_slices(min(S - 2, nk_pad - 2 - kt));
+        lds_barrier();
+      }
     }
-  }
+    mfma_step(av[1], bv[1]);   // last step of the last slice
+  };
+  const int col_first = C::PAIRED ? wn * (C::WN / 2) : wn * C::WN;
+  const int na = col_first >= d.n_valid ? 0 : max(0, min(MI, (d.m_valid - wm * C::WM + 31) / 32));
+  with_count<MI>(__builtin_amdgcn_readfirstlane(na), ring);
   __syncthreads();  // LDS free for the next tile of a persistent worker
 
   epilogue_bf16<C>(g, d, acc, stages, wave, lane);

@@ -94,12 +94,16 @@ hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int 
                        hipStream_t st);
 
 // Fused persistent kernels (bf16).  ws_* are workspace sections.
+// Task cursors of a fused launch: [0] the gather (dispatch_ffn) or combine
+// (ffn_combine) tasks, [1 + x] the GEMM tiles of XCD x's range.
+constexpr int kXcds = 8;
+constexpr int kFusedCursors = 1 + kXcds;
 struct FusedWs {
   int4* mtiles;
   int32_t* n_mtiles;
   int32_t* first_tile;  // [E + Ns]
   int32_t* flags;       // [mt bound]: ready (dispatch_ffn) or done counters (ffn_combine)
-  int32_t* cursor;      // [1]
+  int32_t* cursor;      // [kFusedCursors], right after the flags
   int mt_bound;
   int workers;          // persistent workgroups to launch
 };

@@ -52,7 +52,7 @@ Layout layout(const moe_dims* d) {
   L.mtiles = off;       off = align_up(off + mt * 16);
   L.n_mtiles = off;     off = align_up(off + 16);
   L.first_tile = off;   off = align_up(off + (size_t)(d->E + d->n_shared) * 4);
-  L.flags = off;        off = align_up(off + (mt + 1) * 4);  // flags, then the task cursor
+  L.flags = off;        off = align_up(off + (mt + kFusedCursors) * 4);  // flags, then task cursors
   L.total = off;
   L.mt_bound = (int)mt;
   return L;
