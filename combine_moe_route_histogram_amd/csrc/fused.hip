@@ -1,13 +1,21 @@
 // Fused persistent kernels: Dispatch+GroupGEMM and GroupGEMM+Combine.
 //
 // UniEP article, section 2.1/2.2: one launch per fused stage, a fixed set of
-// persistent workers that take tasks from global atomic cursors -- the
-// communication (here: gather) tasks first, the GroupGEMM tiles after them --
-// and a scoreboard of per-tile readiness flags in global memory that a
-// compute task polls before it starts.  On one GPU the "communication" of
-// dispatch is the gather of token rows into the expert-contiguous buffer, and
-// the relay/arrival part of the scoreboard collapses to one flag per GEMM row
-// tile, set once all its rows are written.
+// persistent workers that take tasks from global atomic cursors, and a
+// scoreboard in global memory that a task polls before it may start.
+//
+// Dispatch+GroupGEMM.  On one GPU the "communication" of dispatch is the
+// gather of token rows into the expert-contiguous order.  MI355X difference
+// from a gather task that GEMM tiles wait for: the direct-to-LDS operand
+// loads take a byte offset per lane, so a tile reads its routed rows straight
+// from the token rows through the slot map; the gather costs nothing extra
+// and no tile waits.  The expert-contiguous copy x_perm (the backward reads
+// it) is written by tasks after the tiles, on workers the tile tail leaves
+// idle.
+//
+// GroupGEMM+Combine.  Combine tasks come after the GEMM tiles; each completed
+// tile adds one to its row tile's counter, and a token is combined once the
+// row tiles of all its rows are complete.
 //
 // MI355X difference from the single cursor of the article: the GEMM tiles are
 // split into 8 contiguous ranges in the plain launch's tile order, one per XCD
@@ -16,11 +24,10 @@
 // from the others.  Tiles that share weight columns and token rows then run
 // on one XCD and share its L2, as in the plain launch.
 //
-// Deadlock freedom: a waiting task only waits on tasks of an earlier phase
-// (GEMM tiles on gathers; combine rows on GEMM tiles), and a worker enters a
-// phase only once every task of the phase before it has been claimed, by a
-// worker that is running and never waits inside that phase, so every wait
-// ends, whatever the number of resident workers.
+// Deadlock freedom: only combine tasks wait, and only on GEMM tiles; a worker
+// takes combine tasks only once every tile has been claimed, by a worker that
+// is running and never waits, so every wait ends, whatever the number of
+// resident workers.
 //
 // Determinism: every GEMM tile runs the same tile code with the same operands
 // as the plain launch and every combine row the same combine code, so the
@@ -90,7 +97,16 @@ __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
   const int n_mt = *w.n_mtiles;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int nvec = g.H / 8;
-  // phase 1: gather tasks -- x_perm rows of one row tile from their tokens
+  // phase 1: GEMM tiles; the routed rows' A operand is gathered from the token
+  // rows as it is loaded (g.a_rows = slot_src), so no tile waits for anything
+  for_tiles_xcd_ranges(w.cursor + 1, n_mt * nt_count, &task_slot, [&](int L) {
+    int tm, tn;
+    band_order(L, n_mt, nt_count, tm, tn);
+    const TileDesc<uint16_t> d = decode_tile<uint16_t, kUp, C::BM, C::BN>(g, tm, tn);
+    run_tile_bf16<C>(g, d, ring);
+  });
+  // phase 2: the permuted copy x_perm (an output the backward reads), one
+  // row tile per task, filling the workers that the tile tail leaves idle
   for (;;) {
     const int task = claim_task(&w.cursor[0], &task_slot);
     if (task >= n_mt) break;
@@ -105,19 +121,7 @@ __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
         for (int v = lane; v < nvec; v += kWave) st16(dst + (int64_t)v * 16, ld16(src + (int64_t)v * 16));
       }
     }
-    publish_set(&w.flags[task]);
   }
-  // phase 2: GEMM tiles, each once its row tile is gathered
-  for_tiles_xcd_ranges(w.cursor + 1, n_mt * nt_count, &task_slot, [&](int L) {
-    int tm, tn;
-    band_order(L, n_mt, nt_count, tm, tn);
-    if (threadIdx.x == 0)
-      while (__hip_atomic_load(&w.flags[tm], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0)
-        __builtin_amdgcn_s_sleep(2);
-    __syncthreads();
-    const TileDesc<uint16_t> d = decode_tile<uint16_t, kUp, C::BM, C::BN>(g, tm, tn);
-    run_tile_bf16<C>(g, d, ring);
-  });
 }
 
 // Row tile of all-rows index `row`: the group from the expert offsets (or the
@@ -184,6 +188,7 @@ hipError_t launch_dispatch_ffn(const GemmArgs& a0, const int32_t* slot_src, cons
   GemmArgs a = a0;
   a.mtiles = w.mtiles;
   a.n_mtiles = w.n_mtiles;
+  a.a_rows = slot_src;
   hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, UpCfg::BM, w.mtiles, w.n_mtiles,
                              w.first_tile, w.flags, w.mt_bound + kFusedCursors, st);
   if (e != hipSuccess) return e;

@@ -50,6 +50,7 @@ struct TileDesc {
   int64_t row0;        // forward kinds: first output row (all-rows index); wgrad: first dW row
   int col0;            // first output column (per half for paired kinds)
   int group;           // expert (>= E: shared expert group - E)
+  const int32_t* a_rows;  // non-null: row m of A is row a_rows[m] of a (gathered rows)
   bool skip;
 };
 
@@ -87,6 +88,7 @@ __device__ inline TileDesc<S> decode_tile(const GemmArgs& g, int tm, int tn) {
   d.skip = false;
   d.ksplit = INT_MAX;
   d.b1 = nullptr;
+  d.a_rows = nullptr;
   const int64_t H = g.H, I = g.I, T = g.T, R = g.R;
   if constexpr (!KindTraits<KIND>::kWgrad) {
     if (tm >= *g.n_mtiles) {
@@ -103,7 +105,14 @@ __device__ inline TileDesc<S> decode_tile(const GemmArgs& g, int tm, int tn) {
     d.row0 = row0;
     d.m_valid = mt.z;
     if constexpr (KIND == kUp) {
-      d.a = shared ? static_cast<const S*>(g.x) + tok0 * H : static_cast<const S*>(g.x_perm) + row0 * H;
+      if (shared) {
+        d.a = static_cast<const S*>(g.x) + tok0 * H;
+      } else if (g.a_rows) {   // dispatch folded into the operand load
+        d.a = static_cast<const S*>(g.x);
+        d.a_rows = g.a_rows + row0;
+      } else {
+        d.a = static_cast<const S*>(g.x_perm) + row0 * H;
+      }
       d.a_sm = H; d.a_sk = 1;
       const S* W1 = shared ? static_cast<const S*>(g.ws1) + sidx * H * I : static_cast<const S*>(g.w1) + (int64_t)grp * H * I;
       const S* W3 = shared ? static_cast<const S*>(g.ws3) + sidx * H * I : static_cast<const S*>(g.w3) + (int64_t)grp * H * I;
@@ -291,8 +300,11 @@ struct DmaOperand {
   static_assert(MN || NH == 1, "KC operands have one source");
   uint32_t off[kPerWave];   // per-lane byte offset (relative to the k slice start) or invalid
   int krow[RAGGED_K ? kPerWave : 1];  // MN with ragged K: k row of this lane
-  // s = row stride (KC) or k stride (MN) in elements; mn_valid per sub-tile.
-  __device__ __forceinline__ void init(int64_t s, int mn_valid, int wave, int lane) {
+  // s = row stride (KC) or k stride (MN) in elements; mn_valid per sub-tile;
+  // rows (KC only, may be null): source row of each tile row, for gathered
+  // operands (the host keeps every such byte offset below 2^31).
+  __device__ __forceinline__ void init(int64_t s, int mn_valid, int wave, int lane,
+                                       const int32_t* rows = nullptr) {
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int q = wave + NW * i;                           // instruction index in the stage
@@ -300,7 +312,12 @@ struct DmaOperand {
         constexpr int kRpi = 1024 / (BK * 2);                 // rows per instruction
         const int r = kRpi * q + lane / kCpr;
         const int c = (lane % kCpr) ^ ((r / (16 / kCpr)) & (kCpr - 1));
-        off[i] = r < mn_valid ? (uint32_t)(r * s * 2 + c * 16) : kBufInvalid;
+        if (r < mn_valid) {
+          const int64_t src = rows ? (int64_t)rows[r] : (int64_t)r;
+          off[i] = (uint32_t)(src * s * 2 + c * 16);
+        } else {
+          off[i] = kBufInvalid;
+        }
       } else {
         constexpr int kQHalf = kHMN * BK * 2 / 1024;         // instructions per sub-tile
         const int qh = q % kQHalf;
@@ -586,7 +603,7 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
   constexpr bool kRagged = KindTraits<C::KIND>::kWgrad;
   DmaOperand<C::BM, C::NW, C::A_MN, 1, kRagged, C::BK> da;
   DmaOperand<C::BN, C::NW, C::B_MN, C::B_NH, kRagged, C::BK> db;
-  if constexpr (C::A_MN) da.init(d.a_sk, d.m_valid, wave, lane); else da.init(d.a_sm, d.m_valid, wave, lane);
+  if constexpr (C::A_MN) da.init(d.a_sk, d.m_valid, wave, lane); else da.init(d.a_sm, d.m_valid, wave, lane, d.a_rows);
   if constexpr (C::B_MN) db.init(d.b_sk, d.n_valid, wave, lane); else db.init(d.b_sn, d.n_valid, wave, lane);
 
   constexpr int BK = C::BK;

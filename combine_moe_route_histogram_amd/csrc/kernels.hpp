@@ -59,6 +59,8 @@ struct GemmArgs {
   const void* dy;
   const void* dout;
   const void* dab;
+  const int32_t* a_rows;  // kUp: token of each routed row, A read from x through it (fused
+                          // dispatch); nullptr: A read from x_perm
   void* o_x_perm;  // fused dispatch: gather target (same buffer as x_perm)
   void* o_out;     // fused combine: token outputs
   void* o_ab;
@@ -102,7 +104,7 @@ struct FusedWs {
   int4* mtiles;
   int32_t* n_mtiles;
   int32_t* first_tile;  // [E + Ns]
-  int32_t* flags;       // [mt bound]: ready (dispatch_ffn) or done counters (ffn_combine)
+  int32_t* flags;       // [mt bound]: done counters of the row tiles (ffn_combine)
   int32_t* cursor;      // [kFusedCursors], right after the flags
   int mt_bound;
   int workers;          // persistent workgroups to launch

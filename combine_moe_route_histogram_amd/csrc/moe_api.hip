@@ -299,10 +299,11 @@ int moe_dispatch_ffn(const moe_dims* d, const void* x, const int32_t* slot_src,
   }
   MOE_TRY(check_ws(d, ws, ws_bytes));
   const hipStream_t st = as_stream(stream);
-  if (d->dtype != MOE_BF16) {
-    // f32 has no persistent kernel: a plain gather and the plain GEMM launch
-    // give the same result
-    MOE_TRY(hip_status(launch_gather(false, x, slot_src, x_perm, d->T * d->K, d->H, st),
+  // f32 has no persistent kernel, and the bf16 one reads token rows with
+  // 32-bit byte offsets: otherwise a plain gather and the plain GEMM launch
+  // give the same result
+  if (d->dtype != MOE_BF16 || (int64_t)d->T * d->H * 2 > 0x7FFF0000LL) {
+    MOE_TRY(hip_status(launch_gather(d->dtype == MOE_BF16, x, slot_src, x_perm, d->T * d->K, d->H, st),
                        "moe_dispatch_ffn (gather)"));
     return moe_expert_ffn_up(d, x_perm, x, offsets, w1, w3, ws1, ws3, ab, h, ws, ws_bytes, stream);
   }
