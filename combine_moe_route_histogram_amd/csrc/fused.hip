@@ -38,19 +38,6 @@
 
 namespace moe {
 
-// The claimed index is broadcast with readfirstlane so the compiler sees it
-// as uniform: every loop around a claim then has a uniform exit.  Otherwise
-// the compiler may treat the exit as divergent and restructure the loop so
-// that thread 0 (which publishes and claims) leaves it while the other lanes
-// go round again on the old index -- a livelock across the barriers.
-__device__ __forceinline__ int claim_task(int32_t* cursor, int* slot) {
-  if (threadIdx.x == 0) *slot = atomicAdd(cursor, 1);
-  __syncthreads();
-  const int task = __builtin_amdgcn_readfirstlane(*slot);
-  __syncthreads();
-  return task;
-}
-
 // Every wave's global stores have reached L2, then one release publishes them.
 // The trailing barrier keeps thread 0's publish and its next claim in separate
 // convergent regions, so the compiler cannot merge them across the loop edge
@@ -67,22 +54,6 @@ __device__ __forceinline__ void publish_add(int32_t* counter) {
   if (threadIdx.x == 0)
     __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-}
-
-// Run every GEMM tile of the ranges, own XCD's range first: tile(L) for the
-// logical tiles L in [0, n).
-template <class F>
-__device__ __forceinline__ void for_tiles_xcd_ranges(int32_t* cursors, int n, int* slot, F&& tile) {
-  const int home = blockIdx.x % kXcds;
-  for (int q = 0; q < kXcds; ++q) {
-    const int r = (home + q) % kXcds;
-    const int lo = (int)((int64_t)n * r / kXcds), hi = (int)((int64_t)n * (r + 1) / kXcds);
-    for (;;) {
-      const int L = lo + claim_task(&cursors[r], slot);
-      if (L >= hi) break;
-      tile(L);
-    }
-  }
 }
 
 using UpCfg = BfPick<kUp>::C;

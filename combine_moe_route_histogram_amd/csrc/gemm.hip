@@ -6,6 +6,8 @@
 // of every group are listed by a one-wave planner straight from the device
 // offsets, so the host never reads a count back.  Tiles never straddle two
 // experts; the last tile of an expert is partial.
+#include <algorithm>
+
 #include "gemm_tile.hpp"
 
 namespace moe {
@@ -64,25 +66,25 @@ hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int 
   return hipGetLastError();
 }
 
-// Launch order -> logical tile.  Workgroups are handed to the 8 XCDs round
-// robin; remapping gives each XCD a contiguous range of logical tiles, so tiles
-// that share weights (same N-tile, consecutive row tiles) share an L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  if (nblocks % 8) return bid;
-  return (bid % 8) * (nblocks / 8) + bid / 8;
-}
-
+// Persistent workers over per-XCD tile ranges (see for_tiles_xcd_ranges).
+// Forward kinds read the number of row tiles from the planner's device output,
+// so the tile count is exact; weight-gradient kinds have a fixed tile grid.
 template <class C>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
-void gemm_bf16_kernel(GemmArgs g, int mt_count, int nt_count) {
+void gemm_bf16_kernel(GemmArgs g, int mt_fixed, int nt_count, int32_t* cursors) {
   MOE_LDS_RING(C, ring);
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  if (L >= mt_count * nt_count) return;
-  int tm, tn;
-  band_order(L, mt_count, nt_count, tm, tn);
-  const TileDesc<uint16_t> d = decode_tile<uint16_t, C::KIND, C::BM, C::BN>(g, tm, tn);
-  if (d.skip) return;
-  run_tile_bf16<C>(g, d, ring);
+  __shared__ int task_slot;
+  const int mt_count = KindTraits<C::KIND>::kWgrad ? mt_fixed : *g.n_mtiles;
+  for_tiles_xcd_ranges(cursors, mt_count * nt_count, &task_slot, [&](int L) {
+    int tm, tn;
+    band_order(L, mt_count, nt_count, tm, tn);
+    const TileDesc<uint16_t> d = decode_tile<uint16_t, C::KIND, C::BM, C::BN>(g, tm, tn);
+    if (!d.skip) run_tile_bf16<C>(g, d, ring);
+  });
+}
+
+__global__ __launch_bounds__(64) void clear_i32_kernel(int32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += 64) p[i] = 0;
 }
 
 template <int KIND>
@@ -98,28 +100,29 @@ __global__ __launch_bounds__(kF32NT) void gemm_f32_kernel(GemmArgs g, int mt_cou
 
 template <int KIND>
 static hipError_t launch_kind(bool is_bf16, GemmArgs a, int4* mtiles_ws, int32_t* n_ws,
-                              hipStream_t st) {
+                              int32_t* cursors, int workers, hipStream_t st) {
   using C = typename BfPick<KIND>::C;
   const int BM = is_bf16 ? C::BM : kF32BM;
   const int BN = is_bf16 ? C::BN : kF32BN;
   int mt_count;
   if constexpr (!KindTraits<KIND>::kWgrad) {
     plan_mtiles_kernel<<<1, 64, 0, st>>>(a.offsets, a.E, a.Ns, a.T, a.R, BM, mtiles_ws, n_ws,
-                                         nullptr, nullptr, 0);
+                                         nullptr, cursors, is_bf16 ? kXcds : 0);
     a.mtiles = mtiles_ws;
     a.n_mtiles = n_ws;
     mt_count = (int)mtile_bound(a.T, a.K, a.E, a.Ns, BM);
     a.mt_max = mt_count;
   } else {
     mt_count = (a.E + a.Ns) * wgrad_mtiles<KIND>(a.H, a.I, BM);
+    if (is_bf16) clear_i32_kernel<<<1, 64, 0, st>>>(cursors, kXcds);
   }
   const int nt_count = gemm_ntiles<KIND>(a.H, a.I, BN);
   const int64_t tiles = (int64_t)mt_count * nt_count;
   if (tiles <= 0) return hipSuccess;
   if (tiles > INT_MAX - 8) return hipErrorInvalidValue;
   if (is_bf16) {
-    const int grid = (int)((tiles + 7) / 8 * 8);
-    gemm_bf16_kernel<C><<<grid, C::NT, 0, st>>>(a, mt_count, nt_count);
+    const int grid = (int)std::min<int64_t>(tiles, workers);
+    gemm_bf16_kernel<C><<<grid, C::NT, 0, st>>>(a, mt_count, nt_count, cursors);
   } else {
     gemm_f32_kernel<KIND><<<(int)tiles, kF32NT, 0, st>>>(a, mt_count, nt_count);
   }
@@ -127,14 +130,14 @@ static hipError_t launch_kind(bool is_bf16, GemmArgs a, int4* mtiles_ws, int32_t
 }
 
 hipError_t launch_gemm(bool is_bf16, int kind, const GemmArgs& a, int4* mtiles_ws,
-                       int32_t* n_mtiles_ws, hipStream_t st) {
+                       int32_t* n_mtiles_ws, int32_t* cursors, int workers, hipStream_t st) {
   switch (kind) {
-    case kUp: return launch_kind<kUp>(is_bf16, a, mtiles_ws, n_mtiles_ws, st);
-    case kDown: return launch_kind<kDown>(is_bf16, a, mtiles_ws, n_mtiles_ws, st);
-    case kBwdUp: return launch_kind<kBwdUp>(is_bf16, a, mtiles_ws, n_mtiles_ws, st);
-    case kBwdDown: return launch_kind<kBwdDown>(is_bf16, a, mtiles_ws, n_mtiles_ws, st);
-    case kWgUp: return launch_kind<kWgUp>(is_bf16, a, mtiles_ws, n_mtiles_ws, st);
-    case kWgDown: return launch_kind<kWgDown>(is_bf16, a, mtiles_ws, n_mtiles_ws, st);
+    case kUp: return launch_kind<kUp>(is_bf16, a, mtiles_ws, n_mtiles_ws, cursors, workers, st);
+    case kDown: return launch_kind<kDown>(is_bf16, a, mtiles_ws, n_mtiles_ws, cursors, workers, st);
+    case kBwdUp: return launch_kind<kBwdUp>(is_bf16, a, mtiles_ws, n_mtiles_ws, cursors, workers, st);
+    case kBwdDown: return launch_kind<kBwdDown>(is_bf16, a, mtiles_ws, n_mtiles_ws, cursors, workers, st);
+    case kWgUp: return launch_kind<kWgUp>(is_bf16, a, mtiles_ws, n_mtiles_ws, cursors, workers, st);
+    case kWgDown: return launch_kind<kWgDown>(is_bf16, a, mtiles_ws, n_mtiles_ws, cursors, workers, st);
     default: return hipErrorInvalidValue;
   }
 }

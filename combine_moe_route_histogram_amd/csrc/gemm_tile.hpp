@@ -839,6 +839,44 @@ __device__ __forceinline__ void band_order(int L, int mt_count, int nt_count, in
   tm = band * kBandM + (rem - tn * rows);
 }
 
+// ------------------------------------------------------- tile scheduling ----
+//
+// Persistent workers (one per CU) take tiles from per-XCD ranges: the tiles,
+// in band order, are split into kXcds contiguous ranges with a cursor each;
+// worker b starts on range b % kXcds (workgroups are handed to the XCDs round
+// robin, so that is its own XCD's range: tiles sharing operands share an L2)
+// and then steals from the other ranges, which evens out the tail.  The
+// claimed index is identical in every thread.
+
+// The claimed index is broadcast with readfirstlane so the compiler sees it
+// as uniform: every loop around a claim then has a uniform exit.  Otherwise
+// the compiler may treat the exit as divergent and restructure the loop so
+// that thread 0 (which publishes and claims) leaves it while the other lanes
+// go round again on the old index -- a livelock across the barriers.
+__device__ __forceinline__ int claim_task(int32_t* cursor, int* slot) {
+  if (threadIdx.x == 0) *slot = atomicAdd(cursor, 1);
+  __syncthreads();
+  const int task = __builtin_amdgcn_readfirstlane(*slot);
+  __syncthreads();
+  return task;
+}
+
+// Run every GEMM tile of the ranges, own XCD's range first: tile(L) for the
+// logical tiles L in [0, n).
+template <class F>
+__device__ __forceinline__ void for_tiles_xcd_ranges(int32_t* cursors, int n, int* slot, F&& tile) {
+  const int home = blockIdx.x % kXcds;
+  for (int q = 0; q < kXcds; ++q) {
+    const int r = (home + q) % kXcds;
+    const int lo = (int)((int64_t)n * r / kXcds), hi = (int)((int64_t)n * (r + 1) / kXcds);
+    for (;;) {
+      const int L = lo + claim_task(&cursors[r], slot);
+      if (L >= hi) break;
+      tile(L);
+    }
+  }
+}
+
 // bf16 tile configurations per kind: BM, BN, waves along M, waves along N,
 // LDS k slices.  The fused kernels use the same ones, so their tiles are
 // computed exactly as by the plain launches.

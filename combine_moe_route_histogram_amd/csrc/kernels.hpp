@@ -85,8 +85,11 @@ inline int64_t mtile_bound(int64_t T, int64_t K, int64_t E, int64_t Ns, int bm) 
 // 64 rows); sizes the row-tile tables in the workspace.
 constexpr int kMinTileM = 64;
 
+// bf16: `workers` persistent workgroups take the tiles through the kXcds
+// cursors at `cursors` (cleared by the launch itself); f32: one workgroup per
+// tile.
 hipError_t launch_gemm(bool is_bf16, int kind, const GemmArgs& a, int4* mtiles_ws,
-                       int32_t* n_mtiles_ws, hipStream_t st);
+                       int32_t* n_mtiles_ws, int32_t* cursors, int workers, hipStream_t st);
 
 // Row-tile planner (one wave): table of bm-row tiles per group, the first
 // table index of every group (if first_tile), and n_clear ints of `clear` set

@@ -113,10 +113,18 @@ GemmArgs base_args(const moe_dims* d, const int32_t* offsets) {
   return a;
 }
 
+int current_cu_count(int* out);
+
+// Plain GEMM launch; the bf16 workers use the tile cursors of the fused
+// kernels' section (never in use by two launches at once: both are ordered on
+// the caller's stream).
 int gemm(const moe_dims* d, int kind, const GemmArgs& a, void* ws, hipStream_t st, const char* what) {
   const Layout L = layout(d);
+  int workers = 0;
+  MOE_TRY(current_cu_count(&workers));
+  int32_t* cursors = ws_at<int32_t>(ws, L.flags) + L.mt_bound + 1;
   return hip_status(launch_gemm(d->dtype == MOE_BF16, kind, a, ws_at<int4>(ws, L.mtiles),
-                                ws_at<int32_t>(ws, L.n_mtiles), st),
+                                ws_at<int32_t>(ws, L.n_mtiles), cursors, workers, st),
                     what);
 }
 
