@@ -72,7 +72,7 @@ __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
   // rows as it is loaded (g.a_rows = slot_src), so no tile waits for anything
   for_tiles_xcd_ranges(w.cursor + 1, n_mt * nt_count, &task_slot, [&](int L) {
     int tm, tn;
-    band_order(L, n_mt, nt_count, tm, tn);
+    band_order_groups(L, nt_count, w.bands, w.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kUp, C::BM, C::BN>(g, tm, tn);
     run_tile_bf16<C>(g, d, ring);
   });
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
   // phase 1: GEMM tiles; each completed tile counts towards its row tile
   for_tiles_xcd_ranges(w.cursor + 1, n_mt * nt_count, &task_slot, [&](int L) {
     int tm, tn;
-    band_order(L, n_mt, nt_count, tm, tn);
+    band_order_groups(L, nt_count, w.bands, w.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kDown, C::BM, C::BN>(g, tm, tn);
     run_tile_bf16<C>(g, d, ring);
     publish_add(&w.flags[tm]);
@@ -159,9 +159,10 @@ hipError_t launch_dispatch_ffn(const GemmArgs& a0, const int32_t* slot_src, cons
   GemmArgs a = a0;
   a.mtiles = w.mtiles;
   a.n_mtiles = w.n_mtiles;
+  a.bands = w.bands;
   a.a_rows = slot_src;
   hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, UpCfg::BM, w.mtiles, w.n_mtiles,
-                             w.first_tile, w.flags, w.mt_bound + kFusedCursors, st);
+                             w.first_tile, w.bands, w.flags, w.mt_bound + kFusedCursors, st);
   if (e != hipSuccess) return e;
   const int nt = gemm_ntiles<kUp>(a.H, a.I, UpCfg::BN);
   dispatch_ffn_kernel<<<w.workers, UpCfg::NT, 0, st>>>(a, slot_src, w, nt);
@@ -173,8 +174,9 @@ hipError_t launch_ffn_combine(const GemmArgs& a0, const int32_t* slot, const flo
   GemmArgs a = a0;
   a.mtiles = w.mtiles;
   a.n_mtiles = w.n_mtiles;
+  a.bands = w.bands;
   hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, DownCfg::BM, w.mtiles, w.n_mtiles,
-                             w.first_tile, w.flags, w.mt_bound + kFusedCursors, st);
+                             w.first_tile, w.bands, w.flags, w.mt_bound + kFusedCursors, st);
   if (e != hipSuccess) return e;
   const int nt = gemm_ntiles<kDown>(a.H, a.I, DownCfg::BN);
   ffn_combine_kernel<<<w.workers, DownCfg::NT, 0, st>>>(a, slot, topk_w, w, nt);

@@ -14,13 +14,16 @@ namespace moe {
 
 // Row-tile table: per group (E routed experts, then Ns shared experts over
 // all T tokens) ceil(rows / bm) entries {group, first row, rows, 0}, groups in
-// order; n_mtiles = number of entries.  One wave: each lane owns a contiguous
-// run of groups, a wave scan gives every lane its first table index.
+// order; n_mtiles[0] = number of entries.  Band table: each group's row tiles
+// in runs of at most kBandM, bands[b] = first row tile of band b, bands[nb] =
+// n_mtiles[0], n_mtiles[1] = nb.  One wave: each lane owns a contiguous run of
+// groups, wave scans give every lane its first table indices.
 __global__ __launch_bounds__(64) void plan_mtiles_kernel(const int32_t* __restrict__ offsets, int E,
                                                          int Ns, int T, int R, int bm,
                                                          int4* __restrict__ mtiles,
                                                          int32_t* __restrict__ n_mtiles,
                                                          int32_t* __restrict__ first_tile,
+                                                         int32_t* __restrict__ bands,
                                                          int32_t* __restrict__ clear, int n_clear) {
   const int lane = threadIdx.x;
   const int G = E + Ns;
@@ -35,34 +38,46 @@ __global__ __launch_bounds__(64) void plan_mtiles_kernel(const int32_t* __restri
       rows = T;
     }
   };
-  int mine = 0;
+  int mine = 0, mine_b = 0;
   for (int grp = g_begin; grp < g_end; ++grp) {
     int row0, rows;
     group_rows(grp, row0, rows);
-    mine += (rows + bm - 1) / bm;
+    const int mt = (rows + bm - 1) / bm;
+    mine += mt;
+    mine_b += (mt + kBandM - 1) / kBandM;
   }
-  int incl = mine;
+  int incl = mine, incl_b = mine_b;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
     const int y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
+    const int yb = __shfl_up(incl_b, o, kWave);
+    if (lane >= o) {
+      incl += y;
+      incl_b += yb;
+    }
   }
-  int idx = incl - mine;
+  int idx = incl - mine, bidx = incl_b - mine_b;
   for (int grp = g_begin; grp < g_end; ++grp) {
     int row0, rows;
     group_rows(grp, row0, rows);
     if (first_tile) first_tile[grp] = idx;
+    const int mt = (rows + bm - 1) / bm;
+    for (int c = 0; c < mt; c += kBandM) bands[bidx++] = idx + c;
     for (int r = 0; r < rows; r += bm) mtiles[idx++] = make_int4(grp, row0 + r, min(bm, rows - r), 0);
   }
-  if (lane == kWave - 1) *n_mtiles = incl;
+  if (lane == kWave - 1) {
+    n_mtiles[0] = incl;
+    n_mtiles[1] = incl_b;
+    bands[incl_b] = incl;
+  }
   for (int i = lane; i < n_clear; i += kWave) clear[i] = 0;
 }
 
 hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int bm, int4* mtiles,
-                       int32_t* n_mtiles, int32_t* first_tile, int32_t* clear, int n_clear,
-                       hipStream_t st) {
+                       int32_t* n_mtiles, int32_t* first_tile, int32_t* bands, int32_t* clear,
+                       int n_clear, hipStream_t st) {
   plan_mtiles_kernel<<<1, 64, 0, st>>>(offsets, E, Ns, T, R, bm, mtiles, n_mtiles, first_tile,
-                                       clear, n_clear);
+                                       bands, clear, n_clear);
   return hipGetLastError();
 }
 
@@ -77,7 +92,10 @@ void gemm_bf16_kernel(GemmArgs g, int mt_fixed, int nt_count, int32_t* cursors) 
   const int mt_count = KindTraits<C::KIND>::kWgrad ? mt_fixed : *g.n_mtiles;
   for_tiles_xcd_ranges(cursors, mt_count * nt_count, &task_slot, [&](int L) {
     int tm, tn;
-    band_order(L, mt_count, nt_count, tm, tn);
+    if constexpr (KindTraits<C::KIND>::kWgrad)
+      band_order(L, mt_count, nt_count, tm, tn);
+    else
+      band_order_groups(L, nt_count, g.bands, g.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, C::KIND, C::BM, C::BN>(g, tm, tn);
     if (!d.skip) run_tile_bf16<C>(g, d, ring);
   });
@@ -100,16 +118,17 @@ __global__ __launch_bounds__(kF32NT) void gemm_f32_kernel(GemmArgs g, int mt_cou
 
 template <int KIND>
 static hipError_t launch_kind(bool is_bf16, GemmArgs a, int4* mtiles_ws, int32_t* n_ws,
-                              int32_t* cursors, int workers, hipStream_t st) {
+                              int32_t* bands_ws, int32_t* cursors, int workers, hipStream_t st) {
   using C = typename BfPick<KIND>::C;
   const int BM = is_bf16 ? C::BM : kF32BM;
   const int BN = is_bf16 ? C::BN : kF32BN;
   int mt_count;
   if constexpr (!KindTraits<KIND>::kWgrad) {
     plan_mtiles_kernel<<<1, 64, 0, st>>>(a.offsets, a.E, a.Ns, a.T, a.R, BM, mtiles_ws, n_ws,
-                                         nullptr, cursors, is_bf16 ? kXcds : 0);
+                                         nullptr, bands_ws, cursors, is_bf16 ? kXcds : 0);
     a.mtiles = mtiles_ws;
     a.n_mtiles = n_ws;
+    a.bands = bands_ws;
     mt_count = (int)mtile_bound(a.T, a.K, a.E, a.Ns, BM);
     a.mt_max = mt_count;
   } else {
@@ -130,16 +149,19 @@ static hipError_t launch_kind(bool is_bf16, GemmArgs a, int4* mtiles_ws, int32_t
 }
 
 hipError_t launch_gemm(bool is_bf16, int kind, const GemmArgs& a, int4* mtiles_ws,
-                       int32_t* n_mtiles_ws, int32_t* cursors, int workers, hipStream_t st) {
+                       int32_t* n_mtiles_ws, int32_t* bands_ws, int32_t* cursors, int workers,
+                       hipStream_t st) {
+#define MOE_KIND(K) launch_kind<K>(is_bf16, a, mtiles_ws, n_mtiles_ws, bands_ws, cursors, workers, st)
   switch (kind) {
-    case kUp: return launch_kind<kUp>(is_bf16, a, mtiles_ws, n_mtiles_ws, cursors, workers, st);
-    case kDown: return launch_kind<kDown>(is_bf16, a, mtiles_ws, n_mtiles_ws, cursors, workers, st);
-    case kBwdUp: return launch_kind<kBwdUp>(is_bf16, a, mtiles_ws, n_mtiles_ws, cursors, workers, st);
-    case kBwdDown: return launch_kind<kBwdDown>(is_bf16, a, mtiles_ws, n_mtiles_ws, cursors, workers, st);
-    case kWgUp: return launch_kind<kWgUp>(is_bf16, a, mtiles_ws, n_mtiles_ws, cursors, workers, st);
-    case kWgDown: return launch_kind<kWgDown>(is_bf16, a, mtiles_ws, n_mtiles_ws, cursors, workers, st);
+    case kUp: return MOE_KIND(kUp);
+    case kDown: return MOE_KIND(kDown);
+    case kBwdUp: return MOE_KIND(kBwdUp);
+    case kBwdDown: return MOE_KIND(kBwdDown);
+    case kWgUp: return MOE_KIND(kWgUp);
+    case kWgDown: return MOE_KIND(kWgDown);
     default: return hipErrorInvalidValue;
   }
+#undef MOE_KIND
 }
 
 }  // namespace moe

@@ -877,6 +877,24 @@ __device__ __forceinline__ void for_tiles_xcd_ranges(int32_t* cursors, int n, in
   }
 }
 
+// Logical tile -> (row tile, column tile) over the planner's bands (a group's
+// row tiles in runs of at most kBandM): bands in order, inside a band the
+// column tiles advance slowest.  Tiles running at the same time on an XCD
+// then belong to one or two experts, so they share weight columns as well as
+// token rows through L2.
+__device__ __forceinline__ void band_order_groups(int L, int nt_count, const int32_t* bands,
+                                                  int n_bands, int& tm, int& tn) {
+  int lo = 0, hi = n_bands;   // the band holding L: largest b with bands[b] * nt_count <= L
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (bands[mid] * nt_count <= L) lo = mid; else hi = mid;
+  }
+  const int first = bands[lo], rows = bands[lo + 1] - first;
+  const int rem = L - first * nt_count;
+  tn = rem / rows;
+  tm = first + (rem - tn * rows);
+}
+
 // bf16 tile configurations per kind: BM, BN, waves along M, waves along N,
 // LDS k slices.  The fused kernels use the same ones, so their tiles are
 // computed exactly as by the plain launches.

@@ -44,7 +44,9 @@ struct GemmArgs {
   int T, H, E, K, I, Ns, R;
   const int32_t* offsets;  // [E+1] routed row ranges
   const int4* mtiles;      // per M-tile {group, first row (all-rows index), rows, 0}
-  const int32_t* n_mtiles; // number of valid entries in mtiles
+  const int32_t* n_mtiles; // [0] valid entries in mtiles, [1] number of bands
+  const int32_t* bands;    // [bands + 1] first M-tile of each band: a group's M-tiles in runs
+                           // of at most kBandM (the last entry is the M-tile count)
   int mt_max;              // host bound on the number of M-tiles
   const void* x_perm;
   const void* x;
@@ -89,13 +91,15 @@ constexpr int kMinTileM = 64;
 // cursors at `cursors` (cleared by the launch itself); f32: one workgroup per
 // tile.
 hipError_t launch_gemm(bool is_bf16, int kind, const GemmArgs& a, int4* mtiles_ws,
-                       int32_t* n_mtiles_ws, int32_t* cursors, int workers, hipStream_t st);
+                       int32_t* n_mtiles_ws, int32_t* bands_ws, int32_t* cursors, int workers,
+                       hipStream_t st);
 
 // Row-tile planner (one wave): table of bm-row tiles per group, the first
 // table index of every group (if first_tile), and n_clear ints of `clear` set
 // to zero (flags and cursors of the fused kernels).
 hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int bm, int4* mtiles,
-                       int32_t* n_mtiles, int32_t* first_tile, int32_t* clear, int n_clear,
+                       int32_t* n_mtiles, int32_t* first_tile, int32_t* bands, int32_t* clear,
+                       int n_clear,
                        hipStream_t st);
 
 // Fused persistent kernels (bf16).  ws_* are workspace sections.
@@ -107,6 +111,7 @@ struct FusedWs {
   int4* mtiles;
   int32_t* n_mtiles;
   int32_t* first_tile;  // [E + Ns]
+  int32_t* bands;       // [mt bound + 1]
   int32_t* flags;       // [mt bound]: done counters of the row tiles (ffn_combine)
   int32_t* cursor;      // [kFusedCursors], right after the flags
   int mt_bound;

@@ -38,7 +38,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace sections (byte offsets).
 struct Layout {
-  size_t chunk_counts, chunk_base, mtiles, n_mtiles, first_tile, flags, total;
+  size_t chunk_counts, chunk_base, mtiles, n_mtiles, bands, first_tile, flags, total;
   int mt_bound;
 };
 
@@ -51,6 +51,7 @@ Layout layout(const moe_dims* d) {
   L.chunk_base = off;   off = align_up(off + nchunk * d->E * 4);
   L.mtiles = off;       off = align_up(off + mt * 16);
   L.n_mtiles = off;     off = align_up(off + 16);
+  L.bands = off;        off = align_up(off + (mt + 1) * 4);
   L.first_tile = off;   off = align_up(off + (size_t)(d->E + d->n_shared) * 4);
   L.flags = off;        off = align_up(off + (mt + kFusedCursors) * 4);  // flags, then task cursors
   L.total = off;
@@ -124,7 +125,8 @@ int gemm(const moe_dims* d, int kind, const GemmArgs& a, void* ws, hipStream_t s
   MOE_TRY(current_cu_count(&workers));
   int32_t* cursors = ws_at<int32_t>(ws, L.flags) + L.mt_bound + 1;
   return hip_status(launch_gemm(d->dtype == MOE_BF16, kind, a, ws_at<int4>(ws, L.mtiles),
-                                ws_at<int32_t>(ws, L.n_mtiles), cursors, workers, st),
+                                ws_at<int32_t>(ws, L.n_mtiles), ws_at<int32_t>(ws, L.bands),
+                                cursors, workers, st),
                     what);
 }
 
@@ -157,6 +159,7 @@ int fused_ws(const moe_dims* d, void* ws, FusedWs* w) {
   w->mtiles = ws_at<int4>(ws, L.mtiles);
   w->n_mtiles = ws_at<int32_t>(ws, L.n_mtiles);
   w->first_tile = ws_at<int32_t>(ws, L.first_tile);
+  w->bands = ws_at<int32_t>(ws, L.bands);
   w->flags = ws_at<int32_t>(ws, L.flags);
   w->cursor = w->flags + L.mt_bound;
   w->mt_bound = L.mt_bound;
