@@ -184,16 +184,22 @@ def main():
             breakdown[k] = {"ms": round(ms, 4), "GB/s": round(rate, 1), "frac": round(rate / PEAK_HBM_GBS, 4)}
     dom = max(per_call_ms, key=per_call_ms.get)
     kind, amount = work[dom]
+    # HBM bytes per launch of the dominant kernel from the committed counter
+    # summary, only if it was taken on the kernel sources being run
+    from combine_moe_route_histogram_amd.profsum import traffic_bytes
+    traffic = traffic_bytes(dom, cfg.name)
     if kind == "mfma":
         peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
         ach = amount / (per_call_ms[dom] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
+                    "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                     "work_per_launch": amount}
     else:
         ach = amount / (per_call_ms[dom] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
+                    "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                     "work_per_launch": amount}
 
     cpu = None

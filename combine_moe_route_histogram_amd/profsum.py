@@ -1,0 +1,195 @@
+"""Text summaries of rocprofv3 output, and the HBM-traffic lookup bench.py uses.
+
+    python -m combine_moe_route_histogram_amd.profsum stats DIR --title T --command C > OUT.md
+    python -m combine_moe_route_histogram_amd.profsum traffic --fetch D1 --write D2 \\
+        --copy-fetch D3 --copy-write D4 --workload W --command-fetch C1 --command-write C2 \\
+        --command-copy-fetch C3 --command-copy-write C4 --out BASE
+
+`stats` reads DIR/*kernel_stats.csv (rocprofv3 --kernel-trace --stats
+--output-format csv) and prints a Markdown table.  `traffic` reads the
+FETCH_SIZE and WRITE_SIZE counter collections of a run of the layer and of
+the copy reference (bench.py --copy-reference: a 256 MiB device copy), derives
+the counter scale factors from the copy, and writes BASE.md (table) and
+BASE.json (per-kernel bytes per dispatch, plus a fingerprint of the kernel
+sources and build flags).  bench.py reports a kernel's traffic only while that
+fingerprint matches the sources it runs, so a kernel changed since its
+counters were taken reports none.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+PROFILES = os.path.join(ROOT, "profiles")
+
+COPY_BYTES = 256 * 1024 * 1024
+
+# bench.py call -> the kernel that does its work (regex on the short kernel name)
+CALL_KERNEL = {
+    "dispatch_ffn": r"^dispatch_ffn_kernel",
+    "ffn_combine": r"^ffn_combine_kernel",
+    "ffn_up": r"^gemm_bf16_kernel<BfCfg<0,",
+    "ffn_down": r"^gemm_bf16_kernel<BfCfg<1,",
+    "ffn_bwd_act": r"^gemm_bf16_kernel<BfCfg<2,",
+    "ffn_bwd_input": r"^gemm_bf16_kernel<BfCfg<3,",
+    "ffn_bwd_wgrad_gate_up": r"^gemm_bf16_kernel<BfCfg<4,",
+    "ffn_bwd_wgrad_down": r"^gemm_bf16_kernel<BfCfg<5,",
+    "dispatch": r"^dispatch_kernel",
+    "combine": r"^combine_kernel",
+    "combine_bwd": r"^combine_bwd_kernel",
+    "dispatch_bwd": r"^dispatch_bwd_kernel",
+}
+
+
+def source_fingerprint() -> str:
+    """sha256 over the kernel sources, the public header and the build flags."""
+    from . import build as B
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")) +
+                   glob.glob(os.path.join(PKG, "csrc", "*.hpp")) +
+                   glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    h.update(" ".join(B.COMMON_FLAGS[1:]).replace(ROOT, "").encode())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    name = re.sub(r"^void ", "", name)
+    name = name.replace("moe::", "")
+    return re.sub(r"\((.*)\)$", "", name).strip()
+
+
+def _one_csv(d: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def kernel_stats(d: str):
+    rows = []
+    with open(_one_csv(d, "kernel_stats.csv")) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((short_name(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
+    rows.sort(key=lambda x: -x[3])
+    return rows
+
+
+def counter_means(d: str, counter: str):
+    """Per kernel: mean counter value per dispatch (KiB for FETCH_SIZE / WRITE_SIZE)."""
+    vals = defaultdict(list)
+    with open(_one_csv(d, "counter_collection.csv")) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                vals[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+
+
+def copy_scale(d: str, counter: str) -> float:
+    """COPY_BYTES divided by what the counter reads for the copy kernel."""
+    means = counter_means(d, counter)
+    cands = {k: v for k, v in means.items() if "copy" in k.lower()}
+    if not cands:
+        raise RuntimeError(f"no copy kernel in {d}")
+    kib = max(v[0] for v in cands.values())
+    return (COPY_BYTES / 1024.0) / kib
+
+
+def cmd_stats(a):
+    rows = kernel_stats(a.dir)
+    out = [f"# {a.title}", "", "Command (from the repository root on an MI355X):", "",
+           f"    {a.command}", ""]
+    if a.note:
+        out += [a.note, ""]
+    out += ["| kernel | calls | avg us | total ms | % |", "|---|---:|---:|---:|---:|"]
+    for n, c, avg, tot, pct in rows:
+        out.append(f"| {n} | {c} | {avg:.1f} | {tot:.2f} | {pct:.2f} |")
+    print("\n".join(out))
+
+
+def cmd_traffic(a):
+    fs = copy_scale(a.copy_fetch, "FETCH_SIZE")
+    ws = copy_scale(a.copy_write, "WRITE_SIZE")
+    fetch = counter_means(a.fetch, "FETCH_SIZE")
+    write = counter_means(a.write, "WRITE_SIZE")
+    kernels = {}
+    for k in sorted(set(fetch) | set(write), key=lambda k: -fetch.get(k, (0, 0))[0]):
+        if k.startswith("at::") or "copyBuffer" in k or "elementwise" in k:
+            continue
+        f, nf = fetch.get(k, (0.0, 0))
+        w, nw = write.get(k, (0.0, 0))
+        kernels[k] = {"fetch_kib_raw": round(f, 1), "write_kib_raw": round(w, 1),
+                      "bytes_read": int(f * 1024 * fs), "bytes_written": int(w * 1024 * ws),
+                      "dispatches": max(nf, nw)}
+    data = {"workload": a.workload, "fingerprint": source_fingerprint(),
+            "fetch_scale": round(fs, 4), "write_scale": round(ws, 4), "kernels": kernels}
+    with open(a.out + ".json", "w") as fh:
+        json.dump(data, fh, indent=1)
+        fh.write("\n")
+    md = [f"# HBM-side traffic per dispatch: {a.workload} layer", "",
+          "Commands (from the repository root on an MI355X; one counter per run):", "",
+          f"    {a.command_fetch}", f"    {a.command_write}", "",
+          f"Calibration: a plain {COPY_BYTES >> 20} MiB device-to-device copy; the counters read "
+          f"x{fs:.2f} (FETCH_SIZE) and x{ws:.2f} (WRITE_SIZE) below the bytes it moves, so the "
+          "raw values are scaled by those factors.  Calibration commands:", "",
+          f"    {a.command_copy_fetch}", f"    {a.command_copy_write}", "",
+          f"Source fingerprint {data['fingerprint']} (kernel sources and build flags).", "",
+          "| kernel | FETCH_SIZE KiB (raw) | read MiB (scaled) | WRITE_SIZE KiB (raw) | written MiB (scaled) |",
+          "|---|---:|---:|---:|---:|"]
+    for k, v in kernels.items():
+        md.append(f"| {k} | {v['fetch_kib_raw']:.0f} | {v['bytes_read'] / 2**20:.1f} | "
+                  f"{v['write_kib_raw']:.0f} | {v['bytes_written'] / 2**20:.1f} |")
+    with open(a.out + ".md", "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    print(f"wrote {a.out}.json and {a.out}.md")
+
+
+def traffic_bytes(call: str, workload: str):
+    """HBM bytes (read + written) per dispatch of the kernel behind `call`, from
+    profiles/<workload>_hbm_traffic.json, or None if absent or taken on other
+    kernel sources."""
+    path = os.path.join(PROFILES, f"{workload}_hbm_traffic.json")
+    pat = CALL_KERNEL.get(call)
+    if not pat or not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        data = json.load(fh)
+    if data.get("fingerprint") != source_fingerprint():
+        return None
+    for k, v in data["kernels"].items():
+        if re.match(pat, k):
+            return v["bytes_read"] + v["bytes_written"]
+    return None
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sp = ap.add_subparsers(dest="cmd", required=True)
+    s = sp.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--title", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--note", default="")
+    t = sp.add_parser("traffic")
+    for n in ("fetch", "write", "copy-fetch", "copy-write", "workload", "out", "command-fetch",
+              "command-write", "command-copy-fetch", "command-copy-write"):
+        t.add_argument("--" + n, required=True)
+    a = ap.parse_args(argv)
+    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    main()
