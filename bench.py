@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="time the unfused forward calls instead of the fused persistent kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--fwd-only", action="store_true")
     ap.add_argument("--copy-reference", action="store_true",
                     help="only run a plain 256 MiB device copy three times (the reference that "
