@@ -48,13 +48,6 @@ __device__ __forceinline__ void publish_set(int32_t* flag) {
   if (threadIdx.x == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
 }
-__device__ __forceinline__ void publish_add(int32_t* counter) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-}
 
 using UpCfg = BfPick<kUp>::C;
 using DownCfg = BfPick<kDown>::C;
@@ -70,11 +63,12 @@ __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
   const int nvec = g.H / 8;
   // phase 1: GEMM tiles; the routed rows' A operand is gathered from the token
   // rows as it is loaded (g.a_rows = slot_src), so no tile waits for anything
-  for_tiles_xcd_ranges(w.cursor + 1, n_mt * nt_count, &task_slot, [&](int L) {
+  for_tasks_xcd_ranges(w.cursor + 1, n_mt * nt_count, 0, 1,
+                       &task_slot, [&](const TaskPart& tp) {
     int tm, tn;
-    band_order_groups(L, nt_count, w.bands, w.n_mtiles[1], tm, tn);
+    band_order_groups(tp.L, nt_count, w.bands, w.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kUp, C::BM, C::BN>(g, tm, tn);
-    run_tile_bf16<C>(g, d, ring);
+    run_tile_bf16<C>(g, d, ring, tp);
   });
   // phase 2: the permuted copy x_perm (an output the backward reads), one
   // row tile per task, filling the workers that the tile tail leaves idle
@@ -124,12 +118,13 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
   const int n_comb = (g.T + kCombineTokens - 1) / kCombineTokens;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   // phase 1: GEMM tiles; each completed tile counts towards its row tile
-  for_tiles_xcd_ranges(w.cursor + 1, n_mt * nt_count, &task_slot, [&](int L) {
+  for_tasks_xcd_ranges(w.cursor + 1, n_mt * nt_count, g.split_wr, (g.I + C::BK - 1) / C::BK,
+                       &task_slot, [&](const TaskPart& tp) {
     int tm, tn;
-    band_order_groups(L, nt_count, w.bands, w.n_mtiles[1], tm, tn);
+    band_order_groups(tp.L, nt_count, w.bands, w.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kDown, C::BM, C::BN>(g, tm, tn);
-    run_tile_bf16<C>(g, d, ring);
-    publish_add(&w.flags[tm]);
+    run_tile_bf16<C>(g, d, ring, tp);
+    if (tp.part == tp.parts - 1) publish_add(&w.flags[tm]);   // the tile is complete
   });
   // phase 2: combine tasks, each token once all its rows' tiles are done
   for (;;) {
@@ -162,7 +157,8 @@ hipError_t launch_dispatch_ffn(const GemmArgs& a0, const int32_t* slot_src, cons
   a.bands = w.bands;
   a.a_rows = slot_src;
   hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, UpCfg::BM, w.mtiles, w.n_mtiles,
-                             w.first_tile, w.bands, w.flags, w.mt_bound + kFusedCursors, st);
+                             w.first_tile, w.bands, w.flags,
+                             w.mt_bound + kFusedCursors + kXcds * kSplitWr, st);
   if (e != hipSuccess) return e;
   const int nt = gemm_ntiles<kUp>(a.H, a.I, UpCfg::BN);
   dispatch_ffn_kernel<<<w.workers, UpCfg::NT, 0, st>>>(a, slot_src, w, nt);
@@ -176,7 +172,8 @@ hipError_t launch_ffn_combine(const GemmArgs& a0, const int32_t* slot, const flo
   a.n_mtiles = w.n_mtiles;
   a.bands = w.bands;
   hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, DownCfg::BM, w.mtiles, w.n_mtiles,
-                             w.first_tile, w.bands, w.flags, w.mt_bound + kFusedCursors, st);
+                             w.first_tile, w.bands, w.flags,
+                             w.mt_bound + kFusedCursors + kXcds * kSplitWr, st);
   if (e != hipSuccess) return e;
   const int nt = gemm_ntiles<kDown>(a.H, a.I, DownCfg::BN);
   ffn_combine_kernel<<<w.workers, DownCfg::NT, 0, st>>>(a, slot, topk_w, w, nt);

@@ -81,23 +81,36 @@ hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int 
   return hipGetLastError();
 }
 
-// Persistent workers over per-XCD tile ranges (see for_tiles_xcd_ranges).
+// k length of the forward-shaped kinds (the same for every tile).
+template <int KIND>
+inline int64_t kind_k_len(const GemmArgs& a) {
+  switch (KIND) {
+    case kUp: return a.H;
+    case kDown: return a.I;
+    case kBwdUp: return a.H;
+    case kBwdDown: return 2 * (int64_t)a.I;
+    default: return 1;   // weight gradient: not split
+  }
+}
+
+// Persistent workers over per-XCD tile ranges (see for_tasks_xcd_ranges).
 // Forward kinds read the number of row tiles from the planner's device output,
 // so the tile count is exact; weight-gradient kinds have a fixed tile grid.
 template <class C>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
-void gemm_bf16_kernel(GemmArgs g, int mt_fixed, int nt_count, int32_t* cursors) {
+void gemm_bf16_kernel(GemmArgs g, int mt_fixed, int nt_count, int32_t* cursors, int max_parts) {
   MOE_LDS_RING(C, ring);
   __shared__ int task_slot;
   const int mt_count = KindTraits<C::KIND>::kWgrad ? mt_fixed : *g.n_mtiles;
-  for_tiles_xcd_ranges(cursors, mt_count * nt_count, &task_slot, [&](int L) {
+  for_tasks_xcd_ranges(cursors, mt_count * nt_count, g.split_wr, max_parts, &task_slot,
+                       [&](const TaskPart& tp) {
     int tm, tn;
     if constexpr (KindTraits<C::KIND>::kWgrad)
-      band_order(L, mt_count, nt_count, tm, tn);
+      band_order(tp.L, mt_count, nt_count, tm, tn);
     else
-      band_order_groups(L, nt_count, g.bands, g.n_mtiles[1], tm, tn);
+      band_order_groups(tp.L, nt_count, g.bands, g.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, C::KIND, C::BM, C::BN>(g, tm, tn);
-    if (!d.skip) run_tile_bf16<C>(g, d, ring);
+    if (!d.skip) run_tile_bf16<C>(g, d, ring, tp);
   });
 }
 
@@ -124,8 +137,10 @@ static hipError_t launch_kind(bool is_bf16, GemmArgs a, int4* mtiles_ws, int32_t
   const int BN = is_bf16 ? C::BN : kF32BN;
   int mt_count;
   if constexpr (!KindTraits<KIND>::kWgrad) {
+    // cursors, then the split counters right after them
     plan_mtiles_kernel<<<1, 64, 0, st>>>(a.offsets, a.E, a.Ns, a.T, a.R, BM, mtiles_ws, n_ws,
-                                         nullptr, bands_ws, cursors, is_bf16 ? kXcds : 0);
+                                         nullptr, bands_ws, cursors,
+                                         is_bf16 ? kXcds + kXcds * kSplitWr : 0);
     a.mtiles = mtiles_ws;
     a.n_mtiles = n_ws;
     a.bands = bands_ws;
@@ -133,15 +148,18 @@ static hipError_t launch_kind(bool is_bf16, GemmArgs a, int4* mtiles_ws, int32_t
     a.mt_max = mt_count;
   } else {
     mt_count = (a.E + a.Ns) * wgrad_mtiles<KIND>(a.H, a.I, BM);
+    a.split_wr = 0;   // many tiles per launch: no tail split
     if (is_bf16) clear_i32_kernel<<<1, 64, 0, st>>>(cursors, kXcds);
   }
+  if (!KindTraits<KIND>::kSplit) a.split_wr = 0;
   const int nt_count = gemm_ntiles<KIND>(a.H, a.I, BN);
   const int64_t tiles = (int64_t)mt_count * nt_count;
   if (tiles <= 0) return hipSuccess;
   if (tiles > INT_MAX - 8) return hipErrorInvalidValue;
   if (is_bf16) {
-    const int grid = (int)std::min<int64_t>(tiles, workers);
-    gemm_bf16_kernel<C><<<grid, C::NT, 0, st>>>(a, mt_count, nt_count, cursors);
+    const int grid = (int)std::min<int64_t>(tiles * kMaxSplit, workers);
+    const int max_parts = (int)((kind_k_len<KIND>(a) + C::BK - 1) / C::BK);
+    gemm_bf16_kernel<C><<<grid, C::NT, 0, st>>>(a, mt_count, nt_count, cursors, max_parts);
   } else {
     gemm_f32_kernel<KIND><<<(int)tiles, kF32NT, 0, st>>>(a, mt_count, nt_count);
   }

@@ -60,6 +60,10 @@ struct KindTraits {
   static constexpr bool kWgrad = (KIND == kWgUp || KIND == kWgDown);
   static constexpr bool kAMn = kWgrad;                        // A is MN-contiguous
   static constexpr bool kBMn = (KIND == kUp || KIND == kDown || kWgrad);  // B is N-contiguous
+  // k split of tail tiles: the kinds with a long k and few column tiles (the
+  // down projection and the input gradient); the others run many rounds of
+  // tiles per launch, where the tail is a small share
+  static constexpr bool kSplit = (KIND == kDown || KIND == kBwdDown);
 };
 
 // Number of N-tiles (per M-tile) and of M-tiles per group for wgrad kinds.
@@ -478,10 +482,17 @@ __device__ __forceinline__ void ld_bf16x4(const void* p, float* v) {
 }
 __device__ __forceinline__ float fast_sigmoid(float a) { return __frcp_rn(1.0f + __expf(-a)); }
 
+// k-split parts: part_out (a helper) receives the tile's partial sums instead
+// of the outputs; part_in[0 .. n_in) (the owner's helpers) are added, in that
+// order, before the outputs are formed.  A partial tile holds, per wave and
+// 32 x 64 staging block, the block's rows of 64 f32 -- the same elements, in
+// the same places, that the epilogue reads back from its LDS region.
 template <class C>
 __device__ __forceinline__ void epilogue_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
                                               const f32x16 (&acc)[C::MI][C::NJ],
-                                              uint8_t* const (&stages)[4], int wave, int lane) {
+                                              uint8_t* const (&stages)[4], int wave, int lane,
+                                              float* part_out, const float* part_in, int n_in,
+                                              int64_t part_floats) {
   constexpr int MI = C::MI, NJ = C::NJ, KIND = C::KIND;
   static_assert(NJ % 2 == 0, "the region takes two 32-column blocks at a time");
   constexpr int kRps = C::STAGE_BYTES / kEpiRegionBytes;   // regions per LDS slice
@@ -510,7 +521,16 @@ __device__ __forceinline__ void epilogue_bf16(const GemmArgs& g, const TileDesc<
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's own region is written
       const int m_base = wm * C::WM + 32 * i;
-      if constexpr (C::PAIRED) {
+      const int64_t pblk = (int64_t)((wave * MI + i) * (NJ / 2) + hc) * (32 * 64);
+      if (KindTraits<KIND>::kSplit && part_out) {   // helper: the block's rows, as staged, to the partial tile
+#pragma unroll
+        for (int pass = 0; pass < 8; ++pass) {
+          const int q = pass * 4 + (lane >> 4);
+          const int c4 = 4 * (lane & 15);
+          *reinterpret_cast<f32x4*>(part_out + pblk + q * 64 + c4) =
+              *reinterpret_cast<const f32x4*>(reg + q * kEpiPitch + c4);
+        }
+      } else if constexpr (C::PAIRED) {
         // 8 lanes per row, 4 columns of both values each; 8 rows per pass
 #pragma unroll
         for (int pass = 0; pass < 4; ++pass) {
@@ -522,6 +542,16 @@ __device__ __forceinline__ void epilogue_bf16(const GemmArgs& g, const TileDesc<
           const float4 vb = *reinterpret_cast<const float4*>(reg + q * kEpiPitch + 32 + c4);
           v[0] = va.x; v[1] = va.y; v[2] = va.z; v[3] = va.w;
           w[0] = vb.x; w[1] = vb.y; w[2] = vb.z; w[3] = vb.w;
+          for (int t = 0; t < (KindTraits<KIND>::kSplit ? n_in : 0); ++t) {
+            const float* pin = part_in + t * part_floats + pblk + q * 64;
+            const f32x4 pa = *reinterpret_cast<const f32x4*>(pin + c4);
+            const f32x4 pb = *reinterpret_cast<const f32x4*>(pin + 32 + c4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] += pa[e];
+              w[e] += pb[e];
+            }
+          }
           if (m < d.m_valid && n < d.n_valid) {
             const int64_t row = d.row0 + m, col = d.col0 + n;
             if constexpr (KIND == kUp) {
@@ -551,6 +581,11 @@ __device__ __forceinline__ void epilogue_bf16(const GemmArgs& g, const TileDesc<
           const int m = m_base + q, n = ncol0 + 64 * hc + c4;
           const float4 va = *reinterpret_cast<const float4*>(reg + q * kEpiPitch + c4);
           float v[4] = {va.x, va.y, va.z, va.w};
+          for (int t = 0; t < (KindTraits<KIND>::kSplit ? n_in : 0); ++t) {
+            const f32x4 pa = *reinterpret_cast<const f32x4*>(part_in + t * part_floats + pblk + q * 64 + c4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += pa[e];
+          }
           if (m < d.m_valid && n < d.n_valid) {
             const int64_t row = d.row0 + m, col = d.col0 + n;
             if constexpr (KIND == kDown) {
@@ -586,11 +621,36 @@ __device__ __forceinline__ void epilogue_bf16(const GemmArgs& g, const TileDesc<
   __syncthreads();  // regions free for the next tile of a persistent worker
 }
 
+// One task of the tile scheduler: a whole tile, or part `part` of `parts`
+// of a tile split along k (see for_tasks_xcd_ranges).
+struct TaskPart {
+  int L;            // logical tile
+  int part, parts;  // parts == 1: the whole tile
+  int slot;         // split tiles: the tile's index among its range's split tiles
+  int range;        // XCD range
+};
+
+// Every wave's global stores have reached L2, then one release publishes them
+// (thread 0, agent scope).  The trailing barrier keeps thread 0's publish and
+// a following claim in separate convergent regions, so the compiler cannot
+// merge them across a loop edge into a thread-0-only path.
+__device__ __forceinline__ void publish_add(int32_t* counter) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+}
+
 // The whole tile: a ring of LDS k slices filled by direct loads, MFMA over
 // each slice with the next k step's fragments in flight, then the epilogue.
+// A split tile's helper part stores its partial sums and publishes them; the
+// owner part (the last) waits for its helpers, adds their partials in part
+// order (a fixed order, so the bits do not depend on timing) and runs the
+// epilogue.
 template <class C>
 __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
-                              uint8_t* const (&stages)[4]) {
+                              uint8_t* const (&stages)[4], const TaskPart& tp) {
   constexpr int MI = C::MI, NJ = C::NJ;
   static_assert(C::STAGES >= 2 && C::STAGES <= 4, "2 to 4 LDS slices");
   const int tid = threadIdx.x;
@@ -607,9 +667,14 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
   if constexpr (C::B_MN) db.init(d.b_sk, d.n_valid, wave, lane); else db.init(d.b_sn, d.n_valid, wave, lane);
 
   constexpr int BK = C::BK;
-  const int nk = (d.k_len + BK - 1) / BK;
-  auto issue = [&](uint8_t* st, int kt) {
-    const int k0 = kt * BK;
+  constexpr bool kSplit = KindTraits<C::KIND>::kSplit;
+  const int parts = kSplit ? tp.parts : 1;
+  const int part = kSplit ? tp.part : 0;
+  const int nk_all = (d.k_len + BK - 1) / BK;
+  const int kb = parts > 1 ? (int)((int64_t)nk_all * part / parts) : 0;   // this part's slices
+  const int nk = parts > 1 ? (int)((int64_t)nk_all * (part + 1) / parts) - kb : nk_all;
+  auto issue = [&](uint8_t* st, int kt) {   // kt: slice index within the part
+    const int k0 = (kb + kt) * BK;
     const bool live = kt < nk;   // kt < nk_pad always; zero-filled past nk
     if constexpr (C::A_MN)
       da.issue(st, d.a + (int64_t)k0 * d.a_sk, nullptr, d.k_len - k0, live, wave);
@@ -743,7 +808,28 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
   with_count<MI>(__builtin_amdgcn_readfirstlane(na), ring);
   __syncthreads();  // LDS free for the next tile of a persistent worker
 
-  epilogue_bf16<C>(g, d, acc, stages, wave, lane);
+  const int64_t tile_floats = (int64_t)C::BM * C::BN;
+  float* part_out = nullptr;
+  const float* part_in = nullptr;
+  int n_in = 0;
+  int32_t* cnt = nullptr;
+  if (kSplit && parts > 1) {
+    float* pbase = g.split_part + (int64_t)(tp.range * kSplitSlots + tp.slot * (parts - 1)) * tile_floats;
+    cnt = g.split_cnt + tp.range * kSplitWr + tp.slot;
+    if (part < parts - 1) {   // helper
+      part_out = pbase + part * tile_floats;
+    } else {                  // owner: wait for the helpers' partials
+      if (threadIdx.x == 0)
+        while (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < parts - 1)
+          __builtin_amdgcn_s_sleep(2);
+      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      part_in = pbase;
+      n_in = parts - 1;
+    }
+  }
+  epilogue_bf16<C>(g, d, acc, stages, wave, lane, part_out, part_in, n_in, tile_floats);
+  if (kSplit && part_out) publish_add(cnt);
 }
 
 // ------------------------------------------------------------------ f32 ----
@@ -861,18 +947,64 @@ __device__ __forceinline__ int claim_task(int32_t* cursor, int* slot) {
   return task;
 }
 
-// Run every GEMM tile of the ranges, own XCD's range first: tile(L) for the
-// logical tiles L in [0, n).
+// Tail split.  A range of n_r < 4 wr tiles worked by wr workers per XCD ends
+// with rem = n_r mod wr tiles that would leave most of the XCD idle; they are
+// split along k into P = min(kMaxSplit, wr / rem, slices) parts when P >= 2,
+// so the range's last round has about as many tasks as workers.  A split
+// tile's parts are consecutive in the range's task order, helpers first and
+// the owner last, so when the owner is claimed every helper has been claimed
+// by a running worker that never waits: the owner's wait always ends.
+struct RangePlan {
+  int lo, hi;        // tiles [lo, hi)
+  int split_from;    // tiles [split_from, hi) are split
+  int parts;
+};
+__device__ __forceinline__ RangePlan range_plan(int r, int n, int wr, int max_parts) {
+  RangePlan p;
+  p.lo = (int)((int64_t)n * r / kXcds);
+  p.hi = (int)((int64_t)n * (r + 1) / kXcds);
+  p.split_from = p.hi;
+  p.parts = 1;
+  if (wr > 0 && p.hi - p.lo < 4 * wr) {   // only ranges of few rounds
+    const int rem = (p.hi - p.lo) % wr;
+    const int P = split_parts(rem, wr, min(max_parts, kMaxSplit));
+    if (P >= 2) {
+      p.split_from = p.hi - rem;
+      p.parts = P;
+    }
+  }
+  return p;
+}
+
+// Run every task of the ranges, own XCD's range first.  wr = 0: whole tiles
+// only; otherwise tail tiles are split as above (max_parts: slices per tile).
 template <class F>
-__device__ __forceinline__ void for_tiles_xcd_ranges(int32_t* cursors, int n, int* slot, F&& tile) {
+__device__ __forceinline__ void for_tasks_xcd_ranges(int32_t* cursors, int n, int wr, int max_parts,
+                                                     int* slot, F&& task) {
   const int home = blockIdx.x % kXcds;
   for (int q = 0; q < kXcds; ++q) {
     const int r = (home + q) % kXcds;
-    const int lo = (int)((int64_t)n * r / kXcds), hi = (int)((int64_t)n * (r + 1) / kXcds);
+    const RangePlan p = range_plan(r, n, wr, max_parts);
+    const int whole = p.split_from - p.lo;
+    const int total = whole + (p.hi - p.split_from) * p.parts;
     for (;;) {
-      const int L = lo + claim_task(&cursors[r], slot);
-      if (L >= hi) break;
-      tile(L);
+      const int t = claim_task(&cursors[r], slot);
+      if (t >= total) break;
+      TaskPart tp;
+      tp.range = r;
+      if (t < whole) {
+        tp.L = p.lo + t;
+        tp.part = 0;
+        tp.parts = 1;
+        tp.slot = 0;
+      } else {
+        const int u = t - whole;
+        tp.slot = u / p.parts;
+        tp.L = p.split_from + tp.slot;
+        tp.part = u - tp.slot * p.parts;
+        tp.parts = p.parts;
+      }
+      task(tp);
     }
   }
 }
@@ -923,6 +1055,12 @@ template <> struct BfPick<kBwdUp> { using C = BfCfg<kBwdUp, MOE_CFG_BWD_UP>; };
 template <> struct BfPick<kBwdDown> { using C = BfCfg<kBwdDown, MOE_CFG_BWD_DOWN>; };
 template <> struct BfPick<kWgUp> { using C = BfCfg<kWgUp, MOE_CFG_WG_UP>; };
 template <> struct BfPick<kWgDown> { using C = BfCfg<kWgDown, MOE_CFG_WG_DOWN>; };
+// the workspace holds k-split partial tiles of at most 256 x 256 f32
+static_assert(BfPick<kUp>::C::BM * BfPick<kUp>::C::BN <= 256 * 256 &&
+                  BfPick<kDown>::C::BM * BfPick<kDown>::C::BN <= 256 * 256 &&
+                  BfPick<kBwdUp>::C::BM * BfPick<kBwdUp>::C::BN <= 256 * 256 &&
+                  BfPick<kBwdDown>::C::BM * BfPick<kBwdDown>::C::BN <= 256 * 256,
+              "partial tile size");
 
 
 }  // namespace moe

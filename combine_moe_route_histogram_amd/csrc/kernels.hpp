@@ -76,7 +76,30 @@ struct GemmArgs {
   float* o_dws1;
   float* o_dws3;
   float* o_dws2;
+  // k split of each XCD range's tail tiles (bf16 forward-shaped kinds)
+  float* split_part;       // [kXcds * kSplitSlots] partial tiles of BM x BN f32
+  int32_t* split_cnt;      // [kXcds * kSplitWr] finished helper parts per split tile
+  int split_wr;            // nominal workers per XCD (0: no split)
 };
+
+// Tail split constants: kSplitWr nominal workers per XCD (256 CUs / 8 XCDs
+// on MI355X; a plan constant, so results do not depend on how many workers
+// actually run), at most kMaxSplit parts per tile, kSplitSlots partial tiles
+// per range = max over rem in [1, kSplitWr) of rem * (parts(rem) - 1).
+constexpr int kSplitWr = 32;
+constexpr int kMaxSplit = 4;
+constexpr int split_parts(int rem, int wr, int max_parts) {
+  return rem <= 0 ? 1 : (wr / rem < max_parts ? wr / rem : max_parts);
+}
+constexpr int split_slots_max() {
+  int m = 0;
+  for (int rem = 1; rem < kSplitWr; ++rem) {
+    const int p = split_parts(rem, kSplitWr, kMaxSplit);
+    if (p >= 2 && rem * (p - 1) > m) m = rem * (p - 1);
+  }
+  return m;
+}
+constexpr int kSplitSlots = split_slots_max();
 
 // Upper bound on the number of row tiles of height bm over all groups.
 inline int64_t mtile_bound(int64_t T, int64_t K, int64_t E, int64_t Ns, int bm) {

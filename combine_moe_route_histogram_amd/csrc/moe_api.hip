@@ -38,7 +38,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace sections (byte offsets).
 struct Layout {
-  size_t chunk_counts, chunk_base, mtiles, n_mtiles, bands, first_tile, flags, total;
+  size_t chunk_counts, chunk_base, mtiles, n_mtiles, bands, first_tile, flags, split, total;
   int mt_bound;
 };
 
@@ -53,7 +53,11 @@ Layout layout(const moe_dims* d) {
   L.n_mtiles = off;     off = align_up(off + 16);
   L.bands = off;        off = align_up(off + (mt + 1) * 4);
   L.first_tile = off;   off = align_up(off + (size_t)(d->E + d->n_shared) * 4);
-  L.flags = off;        off = align_up(off + (mt + kFusedCursors) * 4);  // flags, then task cursors
+  // row-tile counters, then the task cursors, then the split counters
+  L.flags = off;        off = align_up(off + (mt + kFusedCursors + kXcds * kSplitWr) * 4);
+  // partial tiles of the k-split tails (bf16 GEMMs: 256 x 256 f32 each)
+  L.split = off;
+  if (d->dtype == MOE_BF16) off = align_up(off + (size_t)kXcds * kSplitSlots * 256 * 256 * 4);
   L.total = off;
   L.mt_bound = (int)mt;
   return L;
@@ -106,11 +110,17 @@ int check_ws(const moe_dims* d, const void* ws, size_t ws_bytes) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-GemmArgs base_args(const moe_dims* d, const int32_t* offsets) {
+GemmArgs base_args(const moe_dims* d, const int32_t* offsets, void* ws) {
   GemmArgs a{};
   a.T = d->T; a.H = d->H; a.E = d->E; a.K = d->K; a.I = d->I; a.Ns = d->n_shared;
   a.R = d->T * d->K;
   a.offsets = offsets;
+  if (d->dtype == MOE_BF16 && ws) {
+    const Layout L = layout(d);
+    a.split_part = ws_at<float>(ws, L.split);
+    a.split_cnt = ws_at<int32_t>(ws, L.flags) + L.mt_bound + kFusedCursors;
+    a.split_wr = kSplitWr;
+  }
   return a;
 }
 
@@ -251,7 +261,7 @@ int moe_expert_ffn_up(const moe_dims* d, const void* x_perm, const void* x, cons
     MOE_TRY(check_ptr(ws3, "ws3"));
   }
   MOE_TRY(check_ws(d, ws, ws_bytes));
-  GemmArgs a = base_args(d, offsets);
+  GemmArgs a = base_args(d, offsets, ws);
   a.x_perm = x_perm; a.x = x; a.w1 = w1; a.w3 = w3; a.ws1 = ws1; a.ws3 = ws3;
   a.o_ab = ab; a.o_h = h;
   return gemm(d, kUp, a, ws, as_stream(stream), "moe_expert_ffn_up");
@@ -266,7 +276,7 @@ int moe_expert_ffn_down(const moe_dims* d, const void* h, const int32_t* offsets
   MOE_TRY(check_ptr(y, "y"));
   if (d->n_shared) MOE_TRY(check_ptr(ws2, "ws2"));
   MOE_TRY(check_ws(d, ws, ws_bytes));
-  GemmArgs a = base_args(d, offsets);
+  GemmArgs a = base_args(d, offsets, ws);
   a.h = h; a.w2 = w2; a.ws2 = ws2; a.o_y = y;
   return gemm(d, kDown, a, ws, as_stream(stream), "moe_expert_ffn_down");
 }
@@ -318,7 +328,7 @@ int moe_dispatch_ffn(const moe_dims* d, const void* x, const int32_t* slot_src,
                        "moe_dispatch_ffn (gather)"));
     return moe_expert_ffn_up(d, x_perm, x, offsets, w1, w3, ws1, ws3, ab, h, ws, ws_bytes, stream);
   }
-  GemmArgs a = base_args(d, offsets);
+  GemmArgs a = base_args(d, offsets, ws);
   a.x_perm = x_perm; a.o_x_perm = x_perm; a.x = x; a.w1 = w1; a.w3 = w3; a.ws1 = ws1; a.ws3 = ws3;
   a.o_ab = ab; a.o_h = h;
   FusedWs w;
@@ -345,7 +355,7 @@ int moe_ffn_combine(const moe_dims* d, const void* h, const int32_t* offsets, co
     MOE_TRY(moe_expert_ffn_down(d, h, offsets, w2, ws2, y, ws, ws_bytes, stream));
     return moe_combine(d, y, slot, topk_w, out, stream);
   }
-  GemmArgs a = base_args(d, offsets);
+  GemmArgs a = base_args(d, offsets, ws);
   a.h = h; a.w2 = w2; a.ws2 = ws2; a.o_y = y; a.o_out = out;
   FusedWs w;
   MOE_TRY(fused_ws(d, ws, &w));
@@ -380,7 +390,7 @@ int moe_expert_ffn_bwd_act(const moe_dims* d, const void* dy, const void* dout,
     MOE_TRY(check_ptr(ws2, "ws2"));
   }
   MOE_TRY(check_ws(d, ws, ws_bytes));
-  GemmArgs a = base_args(d, offsets);
+  GemmArgs a = base_args(d, offsets, ws);
   a.dy = dy; a.dout = dout; a.w2 = w2; a.ws2 = ws2; a.ab = ab; a.o_dab = dab;
   return gemm(d, kBwdUp, a, ws, as_stream(stream), "moe_expert_ffn_bwd_act");
 }
@@ -399,7 +409,7 @@ int moe_expert_ffn_bwd_input(const moe_dims* d, const void* dab, const int32_t* 
     MOE_TRY(check_ptr(ws3, "ws3"));
   }
   MOE_TRY(check_ws(d, ws, ws_bytes));
-  GemmArgs a = base_args(d, offsets);
+  GemmArgs a = base_args(d, offsets, ws);
   a.dab = dab; a.w1 = w1; a.w3 = w3; a.ws1 = ws1; a.ws3 = ws3; a.o_dx = dx_rows;
   return gemm(d, kBwdDown, a, ws, as_stream(stream), "moe_expert_ffn_bwd_input");
 }
@@ -429,7 +439,7 @@ int moe_expert_ffn_bwd_weight_gate_up(const moe_dims* d, const void* x_perm, con
     MOE_TRY(check_ptr(dws3, "dws3"));
   }
   MOE_TRY(check_ws(d, ws, ws_bytes));
-  GemmArgs a = base_args(d, offsets);
+  GemmArgs a = base_args(d, offsets, ws);
   a.x_perm = x_perm; a.x = x; a.dab = dab;
   a.o_dw1 = dw1; a.o_dw3 = dw3; a.o_dws1 = dws1; a.o_dws3 = dws3;
   return gemm(d, kWgUp, a, ws, as_stream(stream), "moe_expert_ffn_bwd_weight_gate_up");
@@ -448,7 +458,7 @@ int moe_expert_ffn_bwd_weight_down(const moe_dims* d, const void* h, const void*
     MOE_TRY(check_ptr(dws2, "dws2"));
   }
   MOE_TRY(check_ws(d, ws, ws_bytes));
-  GemmArgs a = base_args(d, offsets);
+  GemmArgs a = base_args(d, offsets, ws);
   a.h = h; a.dy = dy; a.dout = dout; a.o_dw2 = dw2; a.o_dws2 = dws2;
   return gemm(d, kWgDown, a, ws, as_stream(stream), "moe_expert_ffn_bwd_weight_down");
 }
