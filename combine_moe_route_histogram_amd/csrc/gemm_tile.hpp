@@ -504,10 +504,38 @@ __device__ __forceinline__ void epilogue_bf16(const GemmArgs& g, const TileDesc<
   const int64_t H = g.H, I = g.I;
   // output column of the wave's first column (paired: of both values)
   const int ncol0 = C::PAIRED ? wn * (C::WN / 2) : wn * C::WN;
+  // activation gradient: the saved a, b of the lane's 8 row pieces of a
+  // 32 x 64 block, loaded one block ahead so that only the first block waits
+  // on a global round trip (a load issued after a block's stores would wait
+  // for them too: stores count in vmcnt)
+  constexpr bool kLoadAB = (KIND == kBwdUp);
+  u32x2 ab_buf[2][8][2];
+  auto load_ab = [&](int i, int hc, u32x2 (&buf)[8][2]) {
+#pragma unroll
+    for (int pass = 0; pass < 8; ++pass) {
+      // unconditional loads (a branch per load would make the compiler's
+      // wait tracking conservative); a lane outside the tile's valid part
+      // reads the tile's first element instead, and its result is not stored
+      int m = wm * C::WM + 32 * i + pass * 4 + (lane >> 4);
+      int n = ncol0 + 64 * hc + 4 * (lane & 15);
+      const bool ok = m < d.m_valid && n < d.n_valid;
+      m = ok ? m : 0;
+      n = ok ? n : 0;
+      const uint16_t* ab = static_cast<const uint16_t*>(g.ab) + (d.row0 + m) * 2 * I + d.col0 + n;
+      buf[pass][0] = *reinterpret_cast<const u32x2*>(ab);
+      buf[pass][1] = *reinterpret_cast<const u32x2*>(ab + I);
+    }
+  };
+  if constexpr (kLoadAB) load_ab(0, 0, ab_buf[0]);
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int hc = 0; hc < NJ / 2; ++hc) {
+      const int blk = i * (NJ / 2) + hc;
+      if constexpr (kLoadAB) {
+        if (blk + 1 < MI * (NJ / 2))
+          load_ab((blk + 1) / (NJ / 2), (blk + 1) % (NJ / 2), ab_buf[(blk + 1) & 1]);
+      }
       // two accumulator blocks -> region columns 0..31 and 32..63: paired
       // kinds take block hc and its partner hc + NJ/2 (same output columns),
       // others two neighbouring blocks
@@ -593,10 +621,9 @@ __device__ __forceinline__ void epilogue_bf16(const GemmArgs& g, const TileDesc<
             } else if constexpr (KIND == kBwdDown) {
               st_bf16x4(static_cast<uint16_t*>(g.o_dx) + row * H + col, v);
             } else if constexpr (KIND == kBwdUp) {
-              const uint16_t* ab = static_cast<const uint16_t*>(g.ab) + row * 2 * I;
               float a[4], b[4], da[4], db[4];
-              ld_bf16x4(ab + col, a);
-              ld_bf16x4(ab + I + col, b);
+              ld_bf16x4(&ab_buf[blk & 1][pass][0], a);
+              ld_bf16x4(&ab_buf[blk & 1][pass][1], b);
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const float sg = fast_sigmoid(a[e]);
