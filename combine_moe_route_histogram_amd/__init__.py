@@ -65,6 +65,9 @@ _SIGS = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_workspace_bytes": (ctypes.c_size_t, [_D]),
     "moe_route": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_route_ranks_workspace_bytes": (ctypes.c_size_t, [_D, ctypes.c_int]),
+    "moe_route_ranks": (ctypes.c_int, [_D, _P, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P,
+                                       ctypes.c_size_t, _P]),
     "moe_dispatch": (ctypes.c_int, [_D, _P, _P, _P, _P]),
     "moe_expert_ffn_up": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_expert_ffn_down": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -171,6 +174,22 @@ def moe_route(d: Dims, logits, topk_idx, topk_w, counts, offsets, slot, slot_src
     wp, wn = _ws(ws)
     _call("moe_route", ctypes.byref(d), _ptr(logits, "logits", torch.float32, T * E),
           _ptr(topk_idx, "topk_idx", torch.int32, T * K), _ptr(topk_w, "topk_w", torch.float32, T * K),
+          _ptr(counts, "counts", torch.int32, E), _ptr(offsets, "offsets", torch.int32, E + 1),
+          _ptr(slot, "slot", torch.int32, T * K), _ptr(slot_src, "slot_src", torch.int32, R),
+          wp, wn, _stream(stream))
+
+
+def moe_route_ranks_workspace_bytes(d: Dims, G: int) -> int:
+    return int(load().moe_route_ranks_workspace_bytes(ctypes.byref(d), int(G)))
+
+
+def moe_route_ranks(d: Dims, topk_idx, G: int, rank_counts, rank_base, counts, offsets, slot,
+                    slot_src, ws, stream=None):
+    T, E, K, R = d.T, d.E, d.K, d.R
+    wp, wn = _ws(ws)
+    _call("moe_route_ranks", ctypes.byref(d), _ptr(topk_idx, "topk_idx", torch.int32, T * K),
+          int(G), _ptr(rank_counts, "rank_counts", torch.int32, G * E),
+          _ptr(rank_base, "rank_base", torch.int32, G * E),
           _ptr(counts, "counts", torch.int32, E), _ptr(offsets, "offsets", torch.int32, E + 1),
           _ptr(slot, "slot", torch.int32, T * K), _ptr(slot_src, "slot_src", torch.int32, R),
           wp, wn, _stream(stream))

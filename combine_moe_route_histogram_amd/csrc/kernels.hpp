@@ -27,6 +27,14 @@ hipError_t launch_combine_bwd(bool is_bf16, const void* dout, const void* y, con
                               hipStream_t st);
 hipError_t launch_dispatch_bwd(bool is_bf16, const void* dx_rows, const int32_t* slot, void* dx,
                                int T, int H, int K, int Ns, hipStream_t st);
+// Algorithm 1 with G explicit ranks (route.hip); chunk scratch sized by
+// route_ranks_nchunk(T, G) chunks.
+int route_ranks_nchunk(int T, int G);
+hipError_t launch_route_ranks(const int32_t* topk_idx, int T, int E, int K, int G,
+                              int32_t* rank_counts, int32_t* rank_base, int32_t* counts,
+                              int32_t* offsets, int32_t* slot, int32_t* slot_src, int32_t* chunk_counts,
+                              int32_t* chunk_base, int32_t* chunk_t0, int32_t* rank_chunk,
+                              hipStream_t st);
 hipError_t launch_route_bwd(const float* dw, const float* w, const int32_t* idx, float* dl, int T,
                             int E, int K, hipStream_t st);
 

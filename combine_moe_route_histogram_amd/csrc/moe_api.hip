@@ -235,6 +235,40 @@ int moe_route(const moe_dims* d, const float* logits, int32_t* topk_idx, float* 
                     "moe_route");
 }
 
+size_t moe_route_ranks_workspace_bytes(const moe_dims* d, int G) {
+  if (check_dims(d) != MOE_OK || G < 1 || G > d->T) return 0;
+  const size_t nmax = (size_t)route_ranks_nchunk(d->T, G);
+  return align_up((2 * nmax * d->E + (nmax + 1) + (size_t)(G + 1)) * 4);
+}
+
+int moe_route_ranks(const moe_dims* d, const int32_t* topk_idx, int G, int32_t* rank_counts,
+                    int32_t* rank_base, int32_t* counts, int32_t* offsets, int32_t* slot,
+                    int32_t* slot_src, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(d));
+  if (G < 1 || G > d->T) return fail(MOE_EINVAL, "G must be in [1, T] (got G=%d, T=%d)", G, d->T);
+  MOE_TRY(check_ptr(topk_idx, "topk_idx"));
+  MOE_TRY(check_ptr(rank_counts, "rank_counts"));
+  MOE_TRY(check_ptr(rank_base, "rank_base"));
+  MOE_TRY(check_ptr(counts, "counts"));
+  MOE_TRY(check_ptr(offsets, "offsets"));
+  MOE_TRY(check_ptr(slot, "slot"));
+  MOE_TRY(check_ptr(slot_src, "slot_src"));
+  const size_t need = moe_route_ranks_workspace_bytes(d, G);
+  if (!ws) return fail(MOE_EWORKSPACE, "workspace is NULL");
+  if (ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "workspace too small: %zu bytes, need %zu", ws_bytes, need);
+  const size_t nmax = (size_t)route_ranks_nchunk(d->T, G);
+  int32_t* w = static_cast<int32_t*>(ws);
+  int32_t* chunk_counts = w;
+  int32_t* chunk_base = chunk_counts + nmax * d->E;
+  int32_t* chunk_t0 = chunk_base + nmax * d->E;
+  int32_t* rank_chunk = chunk_t0 + nmax + 1;
+  return hip_status(launch_route_ranks(topk_idx, d->T, d->E, d->K, G, rank_counts, rank_base, counts,
+                                       offsets, slot, slot_src, chunk_counts, chunk_base, chunk_t0,
+                                       rank_chunk, as_stream(stream)),
+                    "moe_route_ranks");
+}
+
 int moe_dispatch(const moe_dims* d, const void* x, const int32_t* slot, void* x_perm, void* stream) {
   MOE_TRY(check_dims(d));
   MOE_TRY(check_ptr(x, "x"));

@@ -123,9 +123,12 @@ __global__ __launch_bounds__(256) void route_chunk_scan_kernel(const int32_t* __
 // are found with one ballot per bit of the expert id, a lane's rank among
 // them is the popcount of lower peers, and the highest peer advances the
 // expert's running cursor.  slot = offsets[e] + chunk_base[c][e] + rank.
+// chunk_t0 (may be null): chunk c holds tokens [chunk_t0[c], chunk_t0[c+1])
+// instead of the uniform chunks of kChunkTokens.
 __global__ __launch_bounds__(64) void route_slot_kernel(const int32_t* __restrict__ topk_idx,
                                                         const int32_t* __restrict__ counts,
                                                         const int32_t* __restrict__ chunk_base,
+                                                        const int32_t* __restrict__ chunk_t0,
                                                         int T, int E, int K,
                                                         int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ slot,
@@ -158,16 +161,17 @@ __global__ __launch_bounds__(64) void route_slot_kernel(const int32_t* __restric
   if (c == 0 && lane == kWave - 1) offsets[E] = incl;
   __syncthreads();
 
-  const int t0 = c * kChunkTokens;
-  const int t1 = min(T, t0 + kChunkTokens);
+  const int t0 = chunk_t0 ? chunk_t0[c] : c * kChunkTokens;
+  const int t1 = chunk_t0 ? chunk_t0[c + 1] : min(T, t0 + kChunkTokens);
   const int n = (t1 - t0) * K;
   const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
   const uint64_t lower = (1ull << lane) - 1ull;
   const uint64_t higher = ~((2ull << lane) - 1ull);
   for (int q0 = 0; q0 < n; q0 += kWave) {
     const int q = q0 + lane;
-    const bool act = q < n;
-    const int e = act ? topk_idx[(int64_t)t0 * K + q] : 0;
+    const int e_in = q < n ? topk_idx[(int64_t)t0 * K + q] : 0;
+    const bool act = q < n && (unsigned)e_in < (unsigned)E;   // ids outside [0, E) are skipped
+    const int e = act ? e_in : 0;
     uint64_t peers = __ballot(act);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
@@ -211,8 +215,122 @@ hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* topk_
       return hipErrorInvalidValue;
   }
   route_chunk_scan_kernel<<<E, 256, 0, st>>>(chunk_counts, nchunk, E, chunk_base, counts);
-  route_slot_kernel<<<nchunk, 64, 0, st>>>(topk_idx, counts, chunk_base, T, E, K, offsets, slot,
-                                           slot_src);
+  route_slot_kernel<<<nchunk, 64, 0, st>>>(topk_idx, counts, chunk_base, nullptr, T, E, K, offsets,
+                                           slot, slot_src);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- G ranks --
+//
+// Algorithm 1 of the UniEP article (section 2.2) with G explicit ranks, each
+// holding the contiguous token block [floor(T r / G), floor(T (r+1) / G)):
+// every rank counts its own (token, k) pairs per expert, the counts form a
+// [G, E] table (what an all-gather would give each rank), the base offset of
+// rank r in expert e is the expert's start plus the counts of lower ranks,
+// and a pair's slot is its rank's base plus its stable position among the
+// rank's pairs of that expert.  On one GPU each rank is cut into chunks of at
+// most kChunkTokens tokens and the chunk kernels above run over the chunks in
+// rank-major order, so the slots equal the one-rank map by construction.
+
+// Chunk table: chunk_t0[j] = first token of chunk j (chunk_t0[j] = T for the
+// unused chunks up to the bound nmax, and for j = nmax), rank_chunk[r] = first
+// chunk of rank r, rank_chunk[G] = number of chunks.  One block; each thread
+// owns a run of ranks and a block scan places its chunks.
+__global__ __launch_bounds__(256) void rank_chunks_kernel(int T, int G, int nmax,
+                                                          int32_t* __restrict__ chunk_t0,
+                                                          int32_t* __restrict__ rank_chunk) {
+  __shared__ int scan[256];
+  const int tid = threadIdx.x;
+  const int per = (G + 255) / 256;
+  const int r_begin = min(G, tid * per), r_end = min(G, r_begin + per);
+  auto bound = [&](int r) { return (int)(((int64_t)T * r) / G); };
+  int mine = 0;
+  for (int r = r_begin; r < r_end; ++r) mine += (bound(r + 1) - bound(r) + kChunkTokens - 1) / kChunkTokens;
+  scan[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  int j = scan[tid] - mine;
+  for (int r = r_begin; r < r_end; ++r) {
+    rank_chunk[r] = j;
+    for (int t = bound(r); t < bound(r + 1); t += kChunkTokens) chunk_t0[j++] = t;
+  }
+  const int total = scan[255];
+  if (tid == 0) rank_chunk[G] = total;
+  for (int i = total + tid; i <= nmax; i += 256) chunk_t0[i] = T;
+}
+
+// One wave per chunk: the chunk's per-expert pair counts (zero for unused chunks).
+__global__ __launch_bounds__(64) void rank_hist_kernel(const int32_t* __restrict__ topk_idx,
+                                                       const int32_t* __restrict__ chunk_t0, int E,
+                                                       int K, int32_t* __restrict__ chunk_counts) {
+  __shared__ int hist[256];
+  const int c = blockIdx.x, lane = threadIdx.x;
+  for (int e = lane; e < E; e += kWave) hist[e] = 0;
+  __syncthreads();
+  const int t0 = chunk_t0[c], t1 = chunk_t0[c + 1];
+  for (int q = lane; q < (t1 - t0) * K; q += kWave) {
+    const int e = topk_idx[(int64_t)t0 * K + q];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);   // ids outside [0, E) are skipped
+  }
+  __syncthreads();
+  for (int e = lane; e < E; e += kWave) chunk_counts[(int64_t)c * E + e] = hist[e];
+}
+
+// Rank tables from the chunk prefix sums: rank_base[r][e] = expert start +
+// pairs of lower ranks routed to e, rank_counts[r][e] = pairs of rank r routed
+// to e.  Each block scans the expert totals for the starts, then fills its
+// ranks.
+__global__ __launch_bounds__(256) void rank_tables_kernel(const int32_t* __restrict__ counts,
+                                                          const int32_t* __restrict__ chunk_base,
+                                                          const int32_t* __restrict__ rank_chunk,
+                                                          int G, int E, int nmax, int ranks_per_block,
+                                                          int32_t* __restrict__ rank_counts,
+                                                          int32_t* __restrict__ rank_base) {
+  __shared__ int start[256];
+  const int tid = threadIdx.x;
+  start[tid] = tid < E ? counts[tid] : 0;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = tid >= off ? start[tid - off] : 0;
+    __syncthreads();
+    start[tid] += add;
+    __syncthreads();
+  }
+  const int incl = start[tid];
+  __syncthreads();
+  start[tid] = incl - (tid < E ? counts[tid] : 0);   // exclusive
+  __syncthreads();
+  auto cb = [&](int j, int e) { return j < nmax ? chunk_base[(int64_t)j * E + e] : counts[e]; };
+  const int r0 = blockIdx.x * ranks_per_block, r1 = min(G, r0 + ranks_per_block);
+  for (int i = tid; i < (r1 - r0) * E; i += 256) {
+    const int r = r0 + i / E, e = i % E;
+    const int lo = cb(rank_chunk[r], e), hi = cb(rank_chunk[r + 1], e);
+    rank_base[(int64_t)r * E + e] = start[e] + lo;
+    rank_counts[(int64_t)r * E + e] = hi - lo;
+  }
+}
+
+int route_ranks_nchunk(int T, int G) { return (T + kChunkTokens - 1) / kChunkTokens + G; }
+
+hipError_t launch_route_ranks(const int32_t* topk_idx, int T, int E, int K, int G,
+                              int32_t* rank_counts, int32_t* rank_base, int32_t* counts,
+                              int32_t* offsets, int32_t* slot, int32_t* slot_src, int32_t* chunk_counts,
+                              int32_t* chunk_base, int32_t* chunk_t0, int32_t* rank_chunk,
+                              hipStream_t st) {
+  const int nmax = route_ranks_nchunk(T, G);
+  rank_chunks_kernel<<<1, 256, 0, st>>>(T, G, nmax, chunk_t0, rank_chunk);
+  rank_hist_kernel<<<nmax, 64, 0, st>>>(topk_idx, chunk_t0, E, K, chunk_counts);
+  route_chunk_scan_kernel<<<E, 256, 0, st>>>(chunk_counts, nmax, E, chunk_base, counts);
+  const int rpb = 64;
+  rank_tables_kernel<<<(G + rpb - 1) / rpb, 256, 0, st>>>(counts, chunk_base, rank_chunk, G, E, nmax,
+                                                          rpb, rank_counts, rank_base);
+  route_slot_kernel<<<nmax, 64, 0, st>>>(topk_idx, counts, chunk_base, chunk_t0, T, E, K, offsets,
+                                         slot, slot_src);
   return hipGetLastError();
 }
 

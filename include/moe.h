@@ -107,6 +107,28 @@ int moe_route(const moe_dims* d, const float* logits, int32_t* topk_idx, float* 
               int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* slot_src,
               void* ws, size_t ws_bytes, void* stream);
 
+/* Algorithm 1 with G explicit ranks (UniEP section 2.2, "deterministic token
+ * mapping"): rank r holds the contiguous tokens [floor(T r / G),
+ * floor(T (r+1) / G)), 1 <= G <= T.  Every rank counts its own (token, k)
+ * pairs per expert; the counts form a [G, E] table (what an all-gather of the
+ * per-rank histograms gives every rank); the base offset of rank r in expert
+ * e is the expert's start plus the counts of lower ranks; a pair's slot is
+ * its rank's base plus its stable position among its rank's pairs of that
+ * expert.  This is the multi-rank form of the map moe_route builds, and the
+ * slots are identical to it for every G.
+ *  topk_idx    [T, K] i32 in (as moe_route writes it; ids outside [0, E) are
+ *              skipped: they get no slot and are not counted)
+ *  rank_counts [G, E] i32 out: pairs of rank r routed to expert e
+ *  rank_base   [G, E] i32 out: first slot of rank r's pairs in expert e
+ *  counts [E], offsets [E+1], slot [T, K], slot_src [R] i32 out: as moe_route
+ *  ws: device workspace of at least moe_route_ranks_workspace_bytes(d, G)
+ *      bytes (it depends on G; moe_workspace_bytes does not cover it)
+ * Errors: MOE_EINVAL for G outside [1, T] or a NULL array; MOE_EWORKSPACE. */
+size_t moe_route_ranks_workspace_bytes(const moe_dims* d, int G);
+int moe_route_ranks(const moe_dims* d, const int32_t* topk_idx, int G, int32_t* rank_counts,
+                    int32_t* rank_base, int32_t* counts, int32_t* offsets, int32_t* slot,
+                    int32_t* slot_src, void* ws, size_t ws_bytes, void* stream);
+
 /* Dispatch (UniEP 1.1 "scatter"; padding-free layout of section 1.2):
  *  x_perm[slot[t,k]] = x[t];  x [T, H] in, x_perm [R, H] out (bit copy). */
 int moe_dispatch(const moe_dims* d, const void* x, const int32_t* slot, void* x_perm, void* stream);

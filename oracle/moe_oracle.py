@@ -159,6 +159,18 @@ def slot_map(topk_idx: np.ndarray, E: int):
     return counts, offsets, slot, slot_src
 
 
+def rank_base_offsets(counts_rank: np.ndarray) -> np.ndarray:
+    """Algorithm 1's base offsets from the gathered [G, E] count table: rank r's
+    first slot in expert e = the expert's start in the shared buffer (the
+    exclusive prefix of the expert totals) + the counts of lower ranks for e."""
+    c = counts_rank.astype(np.int64)
+    G, E = c.shape
+    total = c.sum(axis=0)
+    expert_start = np.concatenate([[0], np.cumsum(total)[:-1]])
+    lower = np.concatenate([np.zeros((1, E), np.int64), np.cumsum(c, axis=0)[:-1]])
+    return (expert_start[None, :] + lower).astype(np.int32)
+
+
 def slot_map_ranks(topk_idx: np.ndarray, E: int, G: int):
     """Algorithm 1 with G ranks, each holding a contiguous block of tokens.
 
@@ -181,10 +193,7 @@ def slot_map_ranks(topk_idx: np.ndarray, E: int, G: int):
         start = np.concatenate([[0], np.cumsum(counts_rank[r])[:-1]])
         rank_in_expert[order] = np.arange(order.size) - start[sel[order]]
         local.append((sel, rank_in_expert))
-    total = counts_rank.sum(axis=0)
-    expert_start = np.concatenate([[0], np.cumsum(total)[:-1]])
-    base = expert_start[None, :] + np.concatenate([np.zeros((1, E), np.int64),
-                                                   np.cumsum(counts_rank, axis=0)[:-1]])
+    base = rank_base_offsets(counts_rank).astype(np.int64)
     slot = np.empty(T * K, dtype=np.int64)
     for r in range(G):
         sel, rie = local[r]

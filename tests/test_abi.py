@@ -86,3 +86,24 @@ def test_workspace_grows_with_tokens(lib):
     a = lib.moe_workspace_bytes(ctypes.byref(_dims(T=64)))
     b = lib.moe_workspace_bytes(ctypes.byref(_dims(T=131072)))
     assert b > a
+
+
+def test_route_ranks_arguments(lib):
+    d = _dims(T=100)
+    p = ctypes.c_void_p(4096)
+    assert lib.moe_route_ranks_workspace_bytes(ctypes.byref(d), 0) == 0
+    assert lib.moe_route_ranks_workspace_bytes(ctypes.byref(d), 101) == 0
+    w1 = lib.moe_route_ranks_workspace_bytes(ctypes.byref(d), 1)
+    w100 = lib.moe_route_ranks_workspace_bytes(ctypes.byref(d), 100)
+    assert 0 < w1 < w100 and w1 % 256 == 0
+    # G outside [1, T]
+    for G in (0, 101, -3):
+        st = lib.moe_route_ranks(ctypes.byref(d), p, G, p, p, p, p, p, p, p, 1 << 20, None)
+        assert st == 1 and "G must be" in M.moe_last_error()
+    # workspace too small / missing; NULL output
+    st = lib.moe_route_ranks(ctypes.byref(d), p, 4, p, p, p, p, p, p, p, 16, None)
+    assert st == 3
+    st = lib.moe_route_ranks(ctypes.byref(d), p, 4, p, p, p, p, p, p, None, 1 << 20, None)
+    assert st == 3
+    st = lib.moe_route_ranks(ctypes.byref(d), p, 4, None, p, p, p, p, p, p, 1 << 20, None)
+    assert st == 1 and "rank_counts" in M.moe_last_error()

@@ -187,6 +187,19 @@ def test_algorithm1_multirank_equals_single_rank(G):
     counts_rank, slot_g = O.slot_map_ranks(idx, E, G)
     assert counts_rank.shape == (G, E) and counts_rank.sum() == T * K
     assert np.array_equal(slot_g, slot)
+    # base table, brute force: rank r's first slot in expert e is the slot of
+    # its first pair routed to e (when it has one), and consecutive ranks'
+    # bases differ by the lower rank's count; rank 0 starts at the offsets
+    base = O.rank_base_offsets(counts_rank)
+    counts, offsets, _, _ = O.slot_map(idx, E)
+    assert np.array_equal(base[0], offsets[:-1])
+    assert np.array_equal(np.diff(base, axis=0), counts_rank[:-1])
+    bounds = [(T * r) // G for r in range(G + 1)]
+    for r in range(G):
+        for e in range(E):
+            hit = [slot[t, k] for t in range(bounds[r], bounds[r + 1]) for k in range(K) if idx[t, k] == e]
+            if hit:
+                assert min(hit) == base[r, e]
 
 
 # ---------------------------------------------------------------- forward ---
