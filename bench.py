@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--fwd-only", action="store_true")
+    ap.add_argument("--route-ranks", type=int, default=0, metavar="G",
+                    help="instead of the layer, time Algorithm 1 with G explicit ranks "
+                         "(moe_route_ranks) on the workload's routing, beside the oracle")
     ap.add_argument("--copy-reference", action="store_true",
                     help="only run a plain 256 MiB device copy three times (the reference that "
                          "calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -106,6 +109,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     cfg = synth.config(args.workload)
+    if args.route_ranks:
+        bench_route_ranks(args, cfg)
+        return
     backward = ("bwd" in cfg.passes) and not args.fwd_only
     t_gen = time.time()
     inp = synth.make_inputs(cfg, with_grad=backward)
@@ -222,6 +228,62 @@ def main():
         "input_gen_s": round(gen_s, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_route_ranks(args, cfg):
+    """Algorithm 1 with G ranks: moe_route_ranks on the workload's routing."""
+    import numpy as np
+    import torch
+    import synth
+    import combine_moe_route_histogram_amd as M
+    from combine_moe_route_histogram_amd import layer as L
+
+    G = args.route_ranks
+    inp = synth.make_inputs(cfg, with_grad=False)
+    d = L.make_dims(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.n_shared, cfg.dtype)
+    b = L.Buffers(d, backward=False)
+    p = {"logits": synth.to_torch(inp["logits"], "cuda")}
+    L.route(b, p)
+    i32 = lambda n: torch.empty(n, dtype=torch.int32, device="cuda")
+    T, E, K = cfg.T, cfg.E, cfg.K
+    rc, rb, cnt, off, slot, src = i32(G * E), i32(G * E), i32(E), i32(E + 1), i32(T * K), i32(T * K)
+    ws = torch.empty(M.moe_route_ranks_workspace_bytes(d, G), dtype=torch.uint8, device="cuda")
+    call = lambda: M.moe_route_ranks(d, b.topk_idx, G, rc, rb, cnt, off, slot, src, ws)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(c) for a, c in times])) * 1e3
+    assert torch.equal(slot, b.slot.reshape(-1)) and torch.equal(src, b.slot_src.reshape(-1))  # one-rank map
+    nbytes = 3.0 * T * K * 4 + 2.0 * G * E * 4 + 4.0 * (2 * E + 1)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    import oracle as O
+    idx = b.topk_idx.cpu().numpy()
+    t0 = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t0 < 10.0:
+        O.slot_map_ranks(idx, E, G)
+        reps += 1
+    cpu_s = (time.perf_counter() - t0) / reps
+    print(json.dumps({
+        "metric": f"moe_route_ranks latency (Algorithm 1, G={G} ranks)", "value": round(us, 2),
+        "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": False, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={T} E={E} top-{K}, G={G}"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 5), "traffic": None,
+                     "note": "latency-bound: 5 small dependent launches"},
+        "cpu_baseline": {"value": round(cpu_s * 1e6, 1), "unit": "us", "cores": 1, "kind": "oracle",
+                         "sample": f"oracle slot_map_ranks on the same routing, {reps} runs"},
+    }), flush=True)
 
 
 def cpu_baseline(cfg, inp, n_tokens, backward):
