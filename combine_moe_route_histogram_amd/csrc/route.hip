@@ -14,6 +14,10 @@
 
 namespace moe {
 
+__global__ __launch_bounds__(64) void chunk_hist_kernel(const int32_t* __restrict__ topk_idx,
+                                  const int32_t* __restrict__ chunk_t0, int T, int E, int K,
+                                  int32_t* __restrict__ chunk_counts);
+
 // Order-preserving 64-bit key: a larger logit gives a larger key; for equal
 // logits the lower expert id gives the larger key.  -0.0 is folded onto +0.0.
 __device__ __forceinline__ uint64_t route_key(float l, int e) {
@@ -33,61 +37,49 @@ __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > 
 // One group of G lanes per token (G = min(64, next pow2 >= E)); each lane owns
 // up to 4 experts (e = lane + i*G).  K rounds of a group-wide max over the
 // keys pick the experts in descending order.  Block = 256 threads = 4 waves,
-// one block per chunk of kChunkTokens tokens; the chunk's expert histogram is
-// accumulated in LDS (integer adds, order-free) and written to chunk_counts.
+// each wave one group of 64 / G tokens, so a block takes 4 * 64 / G tokens:
+// the per-token rounds are short dependent shuffle chains, and many small
+// blocks keep enough of them in flight to hide their latency.
 template <int G>
-__global__ __launch_bounds__(256) void route_topk_hist_kernel(const float* __restrict__ logits,
-                                                              int T, int E, int K,
-                                                              int32_t* __restrict__ topk_idx,
-                                                              float* __restrict__ topk_w,
-                                                              int32_t* __restrict__ chunk_counts) {
-  __shared__ int hist[256];
-  const int c = blockIdx.x;
-  for (int i = threadIdx.x; i < E; i += blockDim.x) hist[i] = 0;
-  __syncthreads();
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
+                                                         int E, int K, int32_t* __restrict__ topk_idx,
+                                                         float* __restrict__ topk_w) {
   constexpr int TPW = kWave / G;  // tokens per wave
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int gl = lane & (G - 1), grp = lane / G;
-  const int t_begin = c * kChunkTokens;
-  const int t_end = min(T, t_begin + kChunkTokens);
-  for (int tb = t_begin + wave * TPW; tb < t_end; tb += 4 * TPW) {
-    const int t = tb + grp;
-    const bool valid = t < t_end;
-    uint64_t key[4];
+  const int t = (blockIdx.x * 4 + wave) * TPW + grp;
+  const bool valid = t < T;
+  uint64_t key[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = gl + i * G;
-      key[i] = (valid && e < E) ? route_key(logits[(int64_t)t * E + e], e) : 0ull;
+  for (int i = 0; i < 4; ++i) {
+    const int e = gl + i * G;
+    key[i] = (valid && e < E) ? route_key(logits[(int64_t)t * E + e], e) : 0ull;
+  }
+  float l0 = 0.f, zsum = 0.f, my_l = 0.f;
+  int my_e = 0;
+  for (int k = 0; k < K; ++k) {
+    uint64_t best = umax64(umax64(key[0], key[1]), umax64(key[2], key[3]));
+#pragma unroll
+    for (int o = G / 2; o >= 1; o >>= 1) {
+      const uint64_t other = __shfl_xor(best, o, kWave);
+      best = umax64(best, other);
     }
-    float l0 = 0.f, zsum = 0.f, my_l = 0.f;
-    int my_e = 0;
-    for (int k = 0; k < K; ++k) {
-      uint64_t best = umax64(umax64(key[0], key[1]), umax64(key[2], key[3]));
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+    const float l = route_key_logit(best);
 #pragma unroll
-      for (int o = G / 2; o >= 1; o >>= 1) {
-        const uint64_t other = __shfl_xor(best, o, kWave);
-        best = umax64(best, other);
-      }
-      const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-      const float l = route_key_logit(best);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (e == gl + i * G) key[i] = 0ull;  // an expert is picked once
-      if (k == 0) l0 = l;
-      zsum += expf(l - l0);
-      if (gl == k) {
-        my_l = l;
-        my_e = e;
-      }
-    }
-    if (valid && gl < K) {
-      topk_idx[(int64_t)t * K + gl] = my_e;
-      topk_w[(int64_t)t * K + gl] = expf(my_l - l0) / zsum;
-      atomicAdd(&hist[my_e], 1);
+    for (int i = 0; i < 4; ++i)
+      if (e == gl + i * G) key[i] = 0ull;  // an expert is picked once
+    if (k == 0) l0 = l;
+    zsum += expf(l - l0);
+    if (gl == k) {
+      my_l = l;
+      my_e = e;
     }
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < E; i += blockDim.x) chunk_counts[(int64_t)c * E + i] = hist[i];
+  if (valid && gl < K) {
+    topk_idx[(int64_t)t * K + gl] = my_e;
+    topk_w[(int64_t)t * K + gl] = expf(my_l - l0) / zsum;
+  }
 }
 
 // One block per expert: exclusive scan of the expert's column of chunk counts
@@ -196,12 +188,12 @@ hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* topk_
   const int nchunk = route_nchunk(T);
   int g = 1;
   while (g < E && g < 64) g <<= 1;
-  const dim3 grid(nchunk), block(256);
+  const int per_block = 4 * (kWave / g);
+  const dim3 grid((T + per_block - 1) / per_block), block(256);
   switch (g) {
 #define MOE_ROUTE_CASE(G)                                                                      \
   case G:                                                                                      \
-    route_topk_hist_kernel<G><<<grid, block, 0, st>>>(logits, T, E, K, topk_idx, topk_w,       \
-                                                      chunk_counts);                           \
+    route_topk_kernel<G><<<grid, block, 0, st>>>(logits, T, E, K, topk_idx, topk_w);           \
     break;
     MOE_ROUTE_CASE(1)
     MOE_ROUTE_CASE(2)
@@ -214,6 +206,7 @@ hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* topk_
     default:
       return hipErrorInvalidValue;
   }
+  chunk_hist_kernel<<<nchunk, 64, 0, st>>>(topk_idx, nullptr, T, E, K, chunk_counts);
   route_chunk_scan_kernel<<<E, 256, 0, st>>>(chunk_counts, nchunk, E, chunk_base, counts);
   route_slot_kernel<<<nchunk, 64, 0, st>>>(topk_idx, counts, chunk_base, nullptr, T, E, K, offsets,
                                            slot, slot_src);
@@ -264,15 +257,17 @@ __global__ __launch_bounds__(256) void rank_chunks_kernel(int T, int G, int nmax
   for (int i = total + tid; i <= nmax; i += 256) chunk_t0[i] = T;
 }
 
-// One wave per chunk: the chunk's per-expert pair counts (zero for unused chunks).
-__global__ __launch_bounds__(64) void rank_hist_kernel(const int32_t* __restrict__ topk_idx,
-                                                       const int32_t* __restrict__ chunk_t0, int E,
-                                                       int K, int32_t* __restrict__ chunk_counts) {
+// One wave per chunk: the chunk's per-expert pair counts (zero for unused
+// chunks).  chunk_t0 null: uniform chunks of kChunkTokens tokens.
+__global__ __launch_bounds__(64) void chunk_hist_kernel(const int32_t* __restrict__ topk_idx,
+                                                        const int32_t* __restrict__ chunk_t0, int T,
+                                                        int E, int K, int32_t* __restrict__ chunk_counts) {
   __shared__ int hist[256];
   const int c = blockIdx.x, lane = threadIdx.x;
   for (int e = lane; e < E; e += kWave) hist[e] = 0;
   __syncthreads();
-  const int t0 = chunk_t0[c], t1 = chunk_t0[c + 1];
+  const int t0 = chunk_t0 ? chunk_t0[c] : c * kChunkTokens;
+  const int t1 = chunk_t0 ? chunk_t0[c + 1] : min(T, t0 + kChunkTokens);
   for (int q = lane; q < (t1 - t0) * K; q += kWave) {
     const int e = topk_idx[(int64_t)t0 * K + q];
     if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);   // ids outside [0, E) are skipped
@@ -324,7 +319,7 @@ hipError_t launch_route_ranks(const int32_t* topk_idx, int T, int E, int K, int 
                               hipStream_t st) {
   const int nmax = route_ranks_nchunk(T, G);
   rank_chunks_kernel<<<1, 256, 0, st>>>(T, G, nmax, chunk_t0, rank_chunk);
-  rank_hist_kernel<<<nmax, 64, 0, st>>>(topk_idx, chunk_t0, E, K, chunk_counts);
+  chunk_hist_kernel<<<nmax, 64, 0, st>>>(topk_idx, chunk_t0, T, E, K, chunk_counts);
   route_chunk_scan_kernel<<<E, 256, 0, st>>>(chunk_counts, nmax, E, chunk_base, counts);
   const int rpb = 64;
   rank_tables_kernel<<<(G + rpb - 1) / rpb, 256, 0, st>>>(counts, chunk_base, rank_chunk, G, E, nmax,
