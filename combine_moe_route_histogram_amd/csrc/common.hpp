@@ -10,6 +10,7 @@ namespace moe {
 constexpr int kWave = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -69,6 +70,12 @@ template <> struct Elem<uint16_t> {  // bf16
   }
 };
 
+// Lane k's value of v, for a wave-uniform k; unlike a shuffle it also reads
+// lanes that are inactive at this point (e.g. lanes past the end of a row).
+__device__ __forceinline__ int lane_int(int v, int k) { return __builtin_amdgcn_readlane(v, k); }
+__device__ __forceinline__ float lane_float(float v, int k) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
+}
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *static_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *static_cast<u32x4*>(p) = v; }
 

@@ -15,7 +15,9 @@
 //
 // GroupGEMM+Combine.  Combine tasks come after the GEMM tiles; each completed
 // tile adds one to its row tile's counter, and a token is combined once the
-// row tiles of all its rows are complete.
+// row tiles of all its rows are complete.  The tiles write their output rows
+// with agent-coherent stores and publish without a release fence (see
+// publish_add); a combine task takes one acquire after its polls.
 //
 // MI355X difference from the single cursor of the article: the GEMM tiles are
 // split into 8 contiguous ranges in the plain launch's tile order, one per XCD
@@ -37,17 +39,6 @@
 #include "rows.hpp"
 
 namespace moe {
-
-// Every wave's global stores have reached L2, then one release publishes them.
-// The trailing barrier keeps thread 0's publish and its next claim in separate
-// convergent regions, so the compiler cannot merge them across the loop edge
-// into a thread-0-only path (which would split thread 0 off the claim loop).
-__device__ __forceinline__ void publish_set(int32_t* flag) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-}
 
 using UpCfg = BfPick<kUp>::C;
 using DownCfg = BfPick<kDown>::C;
@@ -132,10 +123,12 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
     if (task >= n_comb) break;
     const int t0 = task * kCombineTokens;
     const int t1 = min(g.T, t0 + kCombineTokens);
-    for (int t = t0 + wave; t < t1; t += C::NW) {
-      // the row tiles holding the token's routed rows (q < K) and its
-      // shared-expert rows (q >= K) must all be complete
-      for (int q = lane; q < g.K + g.Ns; q += kWave) {
+    // wave 0 waits until the row tiles holding the task's routed rows (q < K)
+    // and shared-expert rows (q >= K) are all complete, then one acquire
+    if (wave == 0) {
+      const int nq = g.K + g.Ns;
+      for (int i = lane; i < (t1 - t0) * nq; i += kWave) {
+        const int t = t0 + i / nq, q = i - (i / nq) * nq;
         const int64_t row = q < g.K ? (int64_t)slot[(int64_t)t * g.K + q]
                                     : g.R + (int64_t)(q - g.K) * g.T + t;
         const int tile = tile_of_row(row, g, w.first_tile, C::BM);
@@ -143,9 +136,11 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
           __builtin_amdgcn_s_sleep(2);
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    for (int t = t0 + wave; t < t1; t += C::NW)
       combine_row<uint16_t>(static_cast<const uint16_t*>(g.o_y), slot, topk_w,
                             static_cast<uint16_t*>(g.o_out), t, g.T, g.H, g.K, g.Ns, lane);
-    }
   }
 }
 

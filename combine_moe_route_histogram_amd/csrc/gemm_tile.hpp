@@ -475,6 +475,34 @@ __device__ __forceinline__ void st_bf16x4(void* p, const float* v) {
   w[1] = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
   *reinterpret_cast<u32x2*>(p) = w;
 }
+// Stores that other workgroups of the same launch read (the down
+// projection's output rows, which the fused combine reads, and split-k
+// partial sums): relaxed agent-scope atomic stores.  Each is coherent at
+// device scope once it completes (the per-XCD L2 writes it through), so a
+// publish only has to wait for the wave's stores; a release fence would write
+// back the whole L2 of the XCD at every publish.
+__device__ __forceinline__ void st_agent_u64(void* p, uint64_t v) {
+  __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent_bf16x4(void* p, const float* v) {
+  const uint64_t lo = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+  const uint64_t hi = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+  st_agent_u64(p, lo | (hi << 32));
+}
+// Split-k partial tiles: in each 64-float row of a staging block, columns
+// 4j, 4j+1 sit at 2j and columns 4j+2, 4j+3 at 32 + 2j, so each 8-byte store
+// instruction of 16 lanes covers one whole 128-byte line.
+__device__ __forceinline__ void st_part4(float* row, int c4, const f32x4& v) {
+  const int j = c4 >> 2;
+  st_agent_u64(row + 2 * j, (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32));
+  st_agent_u64(row + 32 + 2 * j, (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32));
+}
+__device__ __forceinline__ f32x4 ld_part4(const float* row, int c4) {
+  const int j = c4 >> 2;
+  const f32x2 lo = *reinterpret_cast<const f32x2*>(row + 2 * j);
+  const f32x2 hi = *reinterpret_cast<const f32x2*>(row + 32 + 2 * j);
+  return f32x4{lo[0], lo[1], hi[0], hi[1]};
+}
 __device__ __forceinline__ void ld_bf16x4(const void* p, float* v) {
   const u32x2 w = *reinterpret_cast<const u32x2*>(p);
   v[0] = __uint_as_float(w[0] << 16); v[1] = __uint_as_float(w[0] & 0xFFFF0000u);
@@ -555,8 +583,7 @@ __device__ __forceinline__ void epilogue_bf16(const GemmArgs& g, const TileDesc<
         for (int pass = 0; pass < 8; ++pass) {
           const int q = pass * 4 + (lane >> 4);
           const int c4 = 4 * (lane & 15);
-          *reinterpret_cast<f32x4*>(part_out + pblk + q * 64 + c4) =
-              *reinterpret_cast<const f32x4*>(reg + q * kEpiPitch + c4);
+          st_part4(part_out + pblk + q * 64, c4, *reinterpret_cast<const f32x4*>(reg + q * kEpiPitch + c4));
         }
       } else if constexpr (C::PAIRED) {
         // 8 lanes per row, 4 columns of both values each; 8 rows per pass
@@ -572,8 +599,8 @@ __device__ __forceinline__ void epilogue_bf16(const GemmArgs& g, const TileDesc<
           w[0] = vb.x; w[1] = vb.y; w[2] = vb.z; w[3] = vb.w;
           for (int t = 0; t < (KindTraits<KIND>::kSplit ? n_in : 0); ++t) {
             const float* pin = part_in + t * part_floats + pblk + q * 64;
-            const f32x4 pa = *reinterpret_cast<const f32x4*>(pin + c4);
-            const f32x4 pb = *reinterpret_cast<const f32x4*>(pin + 32 + c4);
+            const f32x4 pa = ld_part4(pin, c4);
+            const f32x4 pb = ld_part4(pin, 32 + c4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               v[e] += pa[e];
@@ -610,14 +637,14 @@ __device__ __forceinline__ void epilogue_bf16(const GemmArgs& g, const TileDesc<
           const float4 va = *reinterpret_cast<const float4*>(reg + q * kEpiPitch + c4);
           float v[4] = {va.x, va.y, va.z, va.w};
           for (int t = 0; t < (KindTraits<KIND>::kSplit ? n_in : 0); ++t) {
-            const f32x4 pa = *reinterpret_cast<const f32x4*>(part_in + t * part_floats + pblk + q * 64 + c4);
+            const f32x4 pa = ld_part4(part_in + t * part_floats + pblk + q * 64, c4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] += pa[e];
           }
           if (m < d.m_valid && n < d.n_valid) {
             const int64_t row = d.row0 + m, col = d.col0 + n;
             if constexpr (KIND == kDown) {
-              st_bf16x4(static_cast<uint16_t*>(g.o_y) + row * H + col, v);
+              st_agent_bf16x4(static_cast<uint16_t*>(g.o_y) + row * H + col, v);
             } else if constexpr (KIND == kBwdDown) {
               st_bf16x4(static_cast<uint16_t*>(g.o_dx) + row * H + col, v);
             } else if constexpr (KIND == kBwdUp) {
@@ -657,15 +684,33 @@ struct TaskPart {
   int range;        // XCD range
 };
 
-// Every wave's global stores have reached L2, then one release publishes them
-// (thread 0, agent scope).  The trailing barrier keeps thread 0's publish and
-// a following claim in separate convergent regions, so the compiler cannot
-// merge them across a loop edge into a thread-0-only path.
+// Publish data written with agent-coherent stores (st_agent_*): every wave
+// waits until its stores have completed (vmcnt 0: each is then coherent at
+// device scope), then thread 0 counts the publish with an agent-scope atomic.
+// No release fence: the data a reader of this counter consumes is coherent
+// already, and a release would write back the XCD's whole L2.  Readers poll
+// the counter and then take one agent-scope acquire (which invalidates their
+// L2's non-coherent lines) before reading.  The trailing barrier keeps thread
+// 0's publish and a following claim in separate convergent regions, so the
+// compiler cannot merge them across a loop edge into a thread-0-only path.
 __device__ __forceinline__ void publish_add(int32_t* counter) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0)
-    __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+}
+
+// Wait until *counter >= n (thread 0 polls with relaxed loads), then one
+// agent-scope acquire in wave 0; the barrier orders the whole workgroup after
+// it.  (An acquiring load per poll would invalidate the L2 at every poll.)
+__device__ __forceinline__ void wait_count(const int32_t* counter, int n) {
+  if (threadIdx.x < kWave) {
+    if (threadIdx.x == 0)
+      while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n)
+        __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
   __syncthreads();
 }
 
@@ -846,11 +891,7 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
     if (part < parts - 1) {   // helper
       part_out = pbase + part * tile_floats;
     } else {                  // owner: wait for the helpers' partials
-      if (threadIdx.x == 0)
-        while (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < parts - 1)
-          __builtin_amdgcn_s_sleep(2);
-      __syncthreads();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      wait_count(cnt, parts - 1);
       part_in = pbase;
       n_in = parts - 1;
     }

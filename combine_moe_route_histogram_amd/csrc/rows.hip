@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kRowBlock) void dispatch_bwd_kernel(const S* __rest
 #pragma unroll
     for (int j = 0; j < P; ++j) acc[j] = 0.f;
     for (int k = 0; k < K; ++k) {
-      const int s = __shfl(my_slot, k, kWave);
+      const int s = lane_int(my_slot, k);
       float f[P];
       Elem<S>::unpack(ld16(reinterpret_cast<const char*>(dx_rows + (int64_t)s * H) + (int64_t)v * 16), f);
 #pragma unroll

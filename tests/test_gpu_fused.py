@@ -21,6 +21,7 @@ SHAPES = [
     (257, 128, 5, 3, 192, 2),
     (520, 192, 16, 4, 128, 0),
     (64, 128, 1, 1, 128, 1),
+    (96, 64, 24, 12, 64, 1),      # 13 rows per token: the combine polls many tiles
 ]
 OUTS = ("x_perm", "ab", "h", "y", "out")
 

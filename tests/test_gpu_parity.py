@@ -26,6 +26,7 @@ SHAPES = [
     (64, 64, 1, 1, 64, 0),        # one expert, one tile
     (1, 128, 4, 2, 128, 0),       # a single token
     (520, 192, 16, 4, 128, 0),    # skewed: empty and huge experts (see logits below)
+    (96, 64, 32, 20, 64, 1),      # more rows per token than 16-byte vectors per row
 ]
 
 
