@@ -471,8 +471,8 @@ constexpr int kEpiRegionBytes = 32 * kEpiPitch * 4;
 
 __device__ __forceinline__ void st_bf16x4(void* p, const float* v) {
   u32x2 w;
-  w[0] = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-  w[1] = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+  w[0] = pack_bf16x2(v[0], v[1]);
+  w[1] = pack_bf16x2(v[2], v[3]);
   *reinterpret_cast<u32x2*>(p) = w;
 }
 // Stores that other workgroups of the same launch read (the down
@@ -485,8 +485,8 @@ __device__ __forceinline__ void st_agent_u64(void* p, uint64_t v) {
   __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_agent_bf16x4(void* p, const float* v) {
-  const uint64_t lo = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-  const uint64_t hi = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+  const uint64_t lo = pack_bf16x2(v[0], v[1]);
+  const uint64_t hi = pack_bf16x2(v[2], v[3]);
   st_agent_u64(p, lo | (hi << 32));
 }
 // Split-k partial tiles: in each 64-float row of a staging block, columns
