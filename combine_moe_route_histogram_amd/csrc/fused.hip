@@ -114,7 +114,7 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
     int tm, tn;
     band_order_groups(tp.L, nt_count, w.bands, w.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kDown, C::BM, C::BN>(g, tm, tn);
-    run_tile_bf16<C>(g, d, ring, tp);
+    run_tile_bf16<C, true>(g, d, ring, tp);
     if (tp.part == tp.parts - 1) publish_add(&w.flags[tm]);   // the tile is complete
   });
   // phase 2: combine tasks, each token once all its rows' tiles are done

@@ -515,7 +515,7 @@ __device__ __forceinline__ float fast_sigmoid(float a) { return __frcp_rn(1.0f +
 // order, before the outputs are formed.  A partial tile holds, per wave and
 // 32 x 64 staging block, the block's rows of 64 f32 -- the same elements, in
 // the same places, that the epilogue reads back from its LDS region.
-template <class C>
+template <class C, bool kCoherentY>
 __device__ __forceinline__ void epilogue_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
                                               const f32x16 (&acc)[C::MI][C::NJ],
                                               uint8_t* const (&stages)[4], int wave, int lane,
@@ -644,7 +644,10 @@ __device__ __forceinline__ void epilogue_bf16(const GemmArgs& g, const TileDesc<
           if (m < d.m_valid && n < d.n_valid) {
             const int64_t row = d.row0 + m, col = d.col0 + n;
             if constexpr (KIND == kDown) {
-              st_agent_bf16x4(static_cast<uint16_t*>(g.o_y) + row * H + col, v);
+              if constexpr (kCoherentY)   // read by other workgroups of the launch
+                st_agent_bf16x4(static_cast<uint16_t*>(g.o_y) + row * H + col, v);
+              else
+                st_bf16x4(static_cast<uint16_t*>(g.o_y) + row * H + col, v);
             } else if constexpr (KIND == kBwdDown) {
               st_bf16x4(static_cast<uint16_t*>(g.o_dx) + row * H + col, v);
             } else if constexpr (KIND == kBwdUp) {
@@ -720,7 +723,7 @@ __device__ __forceinline__ void wait_count(const int32_t* counter, int n) {
 // owner part (the last) waits for its helpers, adds their partials in part
 // order (a fixed order, so the bits do not depend on timing) and runs the
 // epilogue.
-template <class C>
+template <class C, bool kCoherentY = false>
 __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
                               uint8_t* const (&stages)[4], const TaskPart& tp) {
   constexpr int MI = C::MI, NJ = C::NJ;
@@ -896,7 +899,7 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
       n_in = parts - 1;
     }
   }
-  epilogue_bf16<C>(g, d, acc, stages, wave, lane, part_out, part_in, n_in, tile_floats);
+  epilogue_bf16<C, kCoherentY>(g, d, acc, stages, wave, lane, part_out, part_in, n_in, tile_floats);
   if (kSplit && part_out) publish_add(cnt);
 }
 
