@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--unfused", action="store_true",
-                    help="time the unfused forward calls instead of the fused persistent kernels")
+                    help="time the plain calls instead of the fused persistent kernels "
+                         "(dispatch+up, down+combine, and the one-launch backward)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--fwd-only", action="store_true")
@@ -83,6 +84,7 @@ def algorithmic_work(d, b):
         "ffn_bwd_input": ("mfma", gemm(RA, 2)),
         "ffn_bwd_wgrad_gate_up": ("mfma", gemm(RA, 2)),
         "ffn_bwd_wgrad_down": ("mfma", gemm(RA, 1)),
+        "ffn_bwd": ("mfma", gemm(RA, 6)),
         "dispatch_bwd": ("hbm", b * RA * H + b * T * H + 4.0 * R),
         "route_bwd": ("hbm", 12.0 * T * K + 4.0 * T * E),
     }
@@ -149,14 +151,20 @@ def main():
         if backward:
             timed("combine_bwd", M.moe_combine_bwd, d, p["dout"], b.y, b.slot, b.topk_w, b.dy,
                   b.dtopk_w)
-            timed("ffn_bwd_act", M.moe_expert_ffn_bwd_act, d, b.dy, p.get("dout"), b.offsets,
-                  p["w2"], p.get("ws2"), b.ab, b.dab, b.ws)
-            timed("ffn_bwd_input", M.moe_expert_ffn_bwd_input, d, b.dab, b.offsets, p["w1"],
-                  p["w3"], p.get("ws1"), p.get("ws3"), b.dx_rows, b.ws)
-            timed("ffn_bwd_wgrad_gate_up", M.moe_expert_ffn_bwd_weight_gate_up, d, b.x_perm,
-                  p["x"], b.dab, b.offsets, b.dw1, b.dw3, b.dws1, b.dws3, b.ws)
-            timed("ffn_bwd_wgrad_down", M.moe_expert_ffn_bwd_weight_down, d, b.h, b.dy,
-                  p.get("dout"), b.offsets, b.dw2, b.dws2, b.ws)
+            if fused:   # B and W in one launch, W tiles in the gaps of B
+                timed("ffn_bwd", M.moe_expert_ffn_bwd, d, b.dy, p.get("dout"), b.offsets, p["w1"],
+                      p["w3"], p["w2"], p.get("ws1"), p.get("ws3"), p.get("ws2"), b.ab, b.x_perm,
+                      p["x"], b.h, b.dab, b.dx_rows, b.dw1, b.dw3, b.dw2, b.dws1, b.dws3, b.dws2,
+                      b.ws)
+            else:
+                timed("ffn_bwd_act", M.moe_expert_ffn_bwd_act, d, b.dy, p.get("dout"), b.offsets,
+                      p["w2"], p.get("ws2"), b.ab, b.dab, b.ws)
+                timed("ffn_bwd_input", M.moe_expert_ffn_bwd_input, d, b.dab, b.offsets, p["w1"],
+                      p["w3"], p.get("ws1"), p.get("ws3"), b.dx_rows, b.ws)
+                timed("ffn_bwd_wgrad_gate_up", M.moe_expert_ffn_bwd_weight_gate_up, d, b.x_perm,
+                      p["x"], b.dab, b.offsets, b.dw1, b.dw3, b.dws1, b.dws3, b.ws)
+                timed("ffn_bwd_wgrad_down", M.moe_expert_ffn_bwd_weight_down, d, b.h, b.dy,
+                      p.get("dout"), b.offsets, b.dw2, b.dws2, b.ws)
             timed("dispatch_bwd", M.moe_dispatch_bwd, d, b.dx_rows, b.slot, b.dx)
             timed("route_bwd", M.moe_route_bwd, d, b.dtopk_w, b.topk_w, b.topk_idx, b.dlogits)
 

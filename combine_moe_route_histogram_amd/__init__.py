@@ -21,6 +21,7 @@ __all__ = [
     "moe_ffn_combine", "moe_combine_bwd", "moe_expert_ffn_bwd_data",
     "moe_expert_ffn_bwd_weight", "moe_dispatch_bwd", "moe_route_bwd", "moe_expert_ffn_bwd_act",
     "moe_expert_ffn_bwd_input", "moe_expert_ffn_bwd_weight_gate_up", "moe_expert_ffn_bwd_weight_down",
+    "moe_expert_ffn_bwd",
 ]
 
 F32, BF16 = 0, 1
@@ -82,6 +83,7 @@ _SIGS = {
                                                _P, ctypes.c_size_t, _P]),
     "moe_expert_ffn_bwd_weight": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                  _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_expert_ffn_bwd": (ctypes.c_int, [_D] + [_P] * 22 + [ctypes.c_size_t, _P]),
     "moe_expert_ffn_bwd_act": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_expert_ffn_bwd_input": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_expert_ffn_bwd_weight_gate_up": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -294,6 +296,24 @@ def moe_expert_ffn_bwd_weight(d: Dims, x_perm, x, h, dy, dout, dab, offsets, dw1
           _ptr(dw3, "dw3", f32, E * H * I), _ptr(dw2, "dw2", f32, E * I * H),
           _ptr(dws1, "dws1", f32, Ns * H * I), _ptr(dws3, "dws3", f32, Ns * H * I),
           _ptr(dws2, "dws2", f32, Ns * I * H), wp, wn, _stream(stream))
+
+
+def moe_expert_ffn_bwd(d: Dims, dy, dout, offsets, w1, w3, w2, ws1, ws3, ws2, ab, x_perm, x, h,
+                       dab, dx_rows, dw1, dw3, dw2, dws1, dws3, dws2, ws, stream=None):
+    dt, H, I, E, Ns = d.torch_dtype, d.H, d.I, d.E, d.n_shared
+    f32 = torch.float32
+    wp, wn = _ws(ws)
+    _call("moe_expert_ffn_bwd", ctypes.byref(d), _ptr(dy, "dy", dt, d.R * H),
+          _ptr(dout, "dout", dt, d.T * H), _ptr(offsets, "offsets", torch.int32, E + 1),
+          _ptr(w1, "w1", dt, E * H * I), _ptr(w3, "w3", dt, E * H * I), _ptr(w2, "w2", dt, E * I * H),
+          _ptr(ws1, "ws1", dt, Ns * H * I), _ptr(ws3, "ws3", dt, Ns * H * I),
+          _ptr(ws2, "ws2", dt, Ns * I * H), _ptr(ab, "ab", dt, d.RA * 2 * I),
+          _ptr(x_perm, "x_perm", dt, d.R * H), _ptr(x, "x", dt, d.T * H), _ptr(h, "h", dt, d.RA * I),
+          _ptr(dab, "dab", dt, d.RA * 2 * I), _ptr(dx_rows, "dx_rows", dt, d.RA * H),
+          _ptr(dw1, "dw1", f32, E * H * I), _ptr(dw3, "dw3", f32, E * H * I),
+          _ptr(dw2, "dw2", f32, E * I * H), _ptr(dws1, "dws1", f32, Ns * H * I),
+          _ptr(dws3, "dws3", f32, Ns * H * I), _ptr(dws2, "dws2", f32, Ns * I * H), wp, wn,
+          _stream(stream))
 
 
 def moe_expert_ffn_bwd_act(d: Dims, dy, dout, offsets, w2, ws2, ab, dab, ws, stream=None):

@@ -137,10 +137,10 @@ static hipError_t launch_kind(bool is_bf16, GemmArgs a, int4* mtiles_ws, int32_t
   const int BN = is_bf16 ? C::BN : kF32BN;
   int mt_count;
   if constexpr (!KindTraits<KIND>::kWgrad) {
-    // cursors, then the split counters right after them
+    // the tile cursors and, kFusedCursors - 1 ints on, the split counters
     plan_mtiles_kernel<<<1, 64, 0, st>>>(a.offsets, a.E, a.Ns, a.T, a.R, BM, mtiles_ws, n_ws,
                                          nullptr, bands_ws, cursors,
-                                         is_bf16 ? kXcds + kXcds * kSplitWr : 0);
+                                         is_bf16 ? (kFusedCursors - 1) + kXcds * kSplitWr : 0);
     a.mtiles = mtiles_ws;
     a.n_mtiles = n_ws;
     a.bands = bands_ws;

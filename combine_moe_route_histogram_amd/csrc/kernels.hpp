@@ -135,9 +135,12 @@ hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int 
 
 // Fused persistent kernels (bf16).  ws_* are workspace sections.
 // Task cursors of a fused launch: [0] the gather (dispatch_ffn) or combine
-// (ffn_combine) tasks, [1 + x] the GEMM tiles of XCD x's range.
+// (ffn_combine) tasks, or the finished first-phase tiles (ffn_bwd); then
+// kXcds tile cursors per GEMM phase (one phase in the forward kernels, four
+// in ffn_bwd).
 constexpr int kXcds = 8;
-constexpr int kFusedCursors = 1 + kXcds;
+constexpr int kMaxPhases = 4;
+constexpr int kFusedCursors = 1 + kMaxPhases * kXcds;
 struct FusedWs {
   int4* mtiles;
   int32_t* n_mtiles;
@@ -152,5 +155,8 @@ hipError_t launch_dispatch_ffn(const GemmArgs& a, const int32_t* slot_src, const
                                hipStream_t st);
 hipError_t launch_ffn_combine(const GemmArgs& a, const int32_t* slot, const float* topk_w,
                               const FusedWs& w, hipStream_t st);
+// Expert-FFN backward in one persistent launch (bwd.hip): activation-gradient
+// tiles, then dW2 tiles, then input-gradient tiles, then dW1/dW3 tiles.
+hipError_t launch_ffn_bwd(const GemmArgs& a, const FusedWs& w, hipStream_t st);
 
 }  // namespace moe

@@ -507,6 +507,54 @@ int moe_expert_ffn_bwd_weight(const moe_dims* d, const void* x_perm, const void*
   return moe_expert_ffn_bwd_weight_down(d, h, dy, dout, offsets, dw2, dws2, ws, ws_bytes, stream);
 }
 
+int moe_expert_ffn_bwd(const moe_dims* d, const void* dy, const void* dout,
+                       const int32_t* offsets, const void* w1, const void* w3, const void* w2,
+                       const void* ws1, const void* ws3, const void* ws2, const void* ab,
+                       const void* x_perm, const void* x, const void* h, void* dab,
+                       void* dx_rows, float* dw1, float* dw3, float* dw2, float* dws1,
+                       float* dws3, float* dws2, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(d));
+  if (d->dtype != MOE_BF16) {
+    // f32 has no persistent kernel: the plain calls give the same result
+    MOE_TRY(moe_expert_ffn_bwd_data(d, dy, dout, offsets, w1, w3, w2, ws1, ws3, ws2, ab, dab,
+                                    dx_rows, ws, ws_bytes, stream));
+    return moe_expert_ffn_bwd_weight(d, x_perm, x, h, dy, dout, dab, offsets, dw1, dw3, dw2, dws1,
+                                     dws3, dws2, ws, ws_bytes, stream);
+  }
+  MOE_TRY(check_ptr(dy, "dy"));
+  MOE_TRY(check_ptr(offsets, "offsets"));
+  MOE_TRY(check_ptr(w1, "w1"));
+  MOE_TRY(check_ptr(w3, "w3"));
+  MOE_TRY(check_ptr(w2, "w2"));
+  MOE_TRY(check_ptr(ab, "ab"));
+  MOE_TRY(check_ptr(x_perm, "x_perm"));
+  MOE_TRY(check_ptr(h, "h"));
+  MOE_TRY(check_ptr(dab, "dab"));
+  MOE_TRY(check_ptr(dx_rows, "dx_rows"));
+  MOE_TRY(check_ptr(dw1, "dw1"));
+  MOE_TRY(check_ptr(dw3, "dw3"));
+  MOE_TRY(check_ptr(dw2, "dw2"));
+  if (d->n_shared) {
+    MOE_TRY(check_ptr(dout, "dout"));
+    MOE_TRY(check_ptr(x, "x"));
+    MOE_TRY(check_ptr(ws1, "ws1"));
+    MOE_TRY(check_ptr(ws3, "ws3"));
+    MOE_TRY(check_ptr(ws2, "ws2"));
+    MOE_TRY(check_ptr(dws1, "dws1"));
+    MOE_TRY(check_ptr(dws3, "dws3"));
+    MOE_TRY(check_ptr(dws2, "dws2"));
+  }
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  GemmArgs a = base_args(d, offsets, ws);
+  a.dy = dy; a.dout = dout; a.w1 = w1; a.w3 = w3; a.w2 = w2; a.ws1 = ws1; a.ws3 = ws3; a.ws2 = ws2;
+  a.ab = ab; a.x_perm = x_perm; a.x = x; a.h = h; a.dab = dab;
+  a.o_dab = dab; a.o_dx = dx_rows;
+  a.o_dw1 = dw1; a.o_dw3 = dw3; a.o_dw2 = dw2; a.o_dws1 = dws1; a.o_dws3 = dws3; a.o_dws2 = dws2;
+  FusedWs w;
+  MOE_TRY(fused_ws(d, ws, &w));
+  return hip_status(launch_ffn_bwd(a, w, as_stream(stream)), "moe_expert_ffn_bwd");
+}
+
 int moe_dispatch_bwd(const moe_dims* d, const void* dx_rows, const int32_t* slot, void* dx,
                      void* stream) {
   MOE_TRY(check_dims(d));

@@ -10,7 +10,7 @@ from __future__ import annotations
 import torch
 
 from . import (BF16, F32, Dims, moe_combine, moe_combine_bwd, moe_dispatch, moe_dispatch_bwd,
-               moe_dispatch_ffn, moe_expert_ffn_bwd_data, moe_expert_ffn_bwd_weight,
+               moe_dispatch_ffn, moe_expert_ffn_bwd, moe_expert_ffn_bwd_data, moe_expert_ffn_bwd_weight,
                moe_expert_ffn_down, moe_expert_ffn_up, moe_ffn_combine, moe_route, moe_route_bwd,
                moe_workspace_bytes)
 
@@ -77,14 +77,21 @@ def forward(b: Buffers, p: dict, fused: bool = False, stream=None):
         moe_combine(d, b.y, b.slot, b.topk_w, b.out, stream)
 
 
-def backward(b: Buffers, p: dict, stream=None):
-    """combine_bwd -> FFN input grads (B) -> FFN weight grads (W) -> dispatch_bwd -> route_bwd."""
+def backward(b: Buffers, p: dict, fused: bool = False, stream=None):
+    """combine_bwd -> FFN input grads (B) -> FFN weight grads (W) -> dispatch_bwd -> route_bwd.
+    fused: B and W in one launch, W filling the gaps of B (moe_expert_ffn_bwd)."""
     d = b.d
     moe_combine_bwd(d, p["dout"], b.y, b.slot, b.topk_w, b.dy, b.dtopk_w, stream)
-    moe_expert_ffn_bwd_data(d, b.dy, p.get("dout"), b.offsets, p["w1"], p["w3"], p["w2"],
-                            p.get("ws1"), p.get("ws3"), p.get("ws2"), b.ab, b.dab, b.dx_rows,
-                            b.ws, stream)
-    moe_expert_ffn_bwd_weight(d, b.x_perm, p["x"], b.h, b.dy, p.get("dout"), b.dab, b.offsets,
-                              b.dw1, b.dw3, b.dw2, b.dws1, b.dws3, b.dws2, b.ws, stream)
+    if fused:
+        moe_expert_ffn_bwd(d, b.dy, p.get("dout"), b.offsets, p["w1"], p["w3"], p["w2"],
+                           p.get("ws1"), p.get("ws3"), p.get("ws2"), b.ab, b.x_perm, p["x"], b.h,
+                           b.dab, b.dx_rows, b.dw1, b.dw3, b.dw2, b.dws1, b.dws3, b.dws2, b.ws,
+                           stream)
+    else:
+        moe_expert_ffn_bwd_data(d, b.dy, p.get("dout"), b.offsets, p["w1"], p["w3"], p["w2"],
+                                p.get("ws1"), p.get("ws3"), p.get("ws2"), b.ab, b.dab, b.dx_rows,
+                                b.ws, stream)
+        moe_expert_ffn_bwd_weight(d, b.x_perm, p["x"], b.h, b.dy, p.get("dout"), b.dab, b.offsets,
+                                  b.dw1, b.dw3, b.dw2, b.dws1, b.dws3, b.dws2, b.ws, stream)
     moe_dispatch_bwd(d, b.dx_rows, b.slot, b.dx, stream)
     moe_route_bwd(d, b.dtopk_w, b.topk_w, b.topk_idx, b.dlogits, stream)

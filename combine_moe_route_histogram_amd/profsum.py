@@ -37,6 +37,7 @@ COPY_BYTES = 256 * 1024 * 1024
 CALL_KERNEL = {
     "dispatch_ffn": r"^dispatch_ffn_kernel",
     "ffn_combine": r"^ffn_combine_kernel",
+    "ffn_bwd": r"^ffn_bwd_kernel",
     "ffn_up": r"^gemm_bf16_kernel<BfCfg<0,",
     "ffn_down": r"^gemm_bf16_kernel<BfCfg<1,",
     "ffn_bwd_act": r"^gemm_bf16_kernel<BfCfg<2,",

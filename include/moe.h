@@ -237,6 +237,23 @@ int moe_expert_ffn_bwd_weight_down(const moe_dims* d, const void* h, const void*
                                    const void* dout, const int32_t* offsets, float* dw2,
                                    float* dws2, void* ws, size_t ws_bytes, void* stream);
 
+/* The whole expert-FFN backward, B and W, in one persistent launch, with the
+ * weight-gradient GEMMs scheduled into the gaps of the input-gradient chain
+ * (zero-bubble "B/W" split, GraphPP section 2 / 5.1: W needs only operands
+ * that already exist, so it fills bubbles).  Phases of tiles, each one
+ * filling the tail of the one before: dh -> dab (B), dW2 (W), dx_rows from dab
+ * (B), dW1/dW3 from dab (W).  Outputs are bit-identical to
+ * moe_expert_ffn_bwd_data followed by moe_expert_ffn_bwd_weight, for any
+ * number of workers.  Arguments: the union of those two calls (same layouts
+ * and ownership); dab is written and read back inside the call.  f32 runs the
+ * two plain calls.  Errors as for the two calls. */
+int moe_expert_ffn_bwd(const moe_dims* d, const void* dy, const void* dout,
+                       const int32_t* offsets, const void* w1, const void* w3, const void* w2,
+                       const void* ws1, const void* ws3, const void* ws2, const void* ab,
+                       const void* x_perm, const void* x, const void* h, void* dab,
+                       void* dx_rows, float* dw1, float* dw3, float* dw2, float* dws1,
+                       float* dws3, float* dws2, void* ws, size_t ws_bytes, void* stream);
+
 /* Dispatch backward: dx[t] = sum_k dx_rows[slot[t,k]] + sum_s dx_rows[R+s*T+t]
  * (float32 accumulation in that order, one rounding).
  *  dx_rows [RA, H] in, dx [T, H] out. */

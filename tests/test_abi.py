@@ -35,6 +35,27 @@ def test_every_declared_symbol_is_exported(lib):
         assert callable(getattr(M, n)), n
 
 
+def declared_arity():
+    """Number of parameters of every function declared in the header."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for name, params in re.findall(r"\b(moe_[a-z_]+)\s*\(([^)]*)\)\s*;", src):
+        params = params.strip()
+        out[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_signatures_match_header():
+    """ctypes passes arguments beyond argtypes with default conversion (a
+    pointer would be cut to 32 bits), so every binding must declare exactly
+    the header's parameter count."""
+    arity = declared_arity()
+    assert len(arity) >= 17
+    for name, n in arity.items():
+        assert name in M._SIGS, name
+        assert len(M._SIGS[name][1]) == n, (name, len(M._SIGS[name][1]), n)
+
+
 def test_status_strings(lib):
     assert M.moe_status_str(0) == "MOE_OK"
     assert M.moe_status_str(3) == "MOE_EWORKSPACE"
@@ -80,6 +101,28 @@ def test_null_misaligned_and_workspace_errors(lib):
     d2 = _dims(n_shared=2)
     st = lib.moe_expert_ffn_up(ctypes.byref(d2), p, p, p, p, p, None, p, p, p, p, 1 << 30, None)
     assert st == 1
+
+
+def test_fused_bwd_argument_errors(lib):
+    """moe_expert_ffn_bwd checks its pointers and workspace before any launch."""
+    d = _dims()
+    need = lib.moe_workspace_bytes(ctypes.byref(d))
+    p = ctypes.c_void_p(4096)
+    args = [p] * 21
+    args[2] = None                                   # offsets
+    st = lib.moe_expert_ffn_bwd(ctypes.byref(d), *args, p, need, None)
+    assert st == 1 and "offsets" in M.moe_last_error()
+    args = [p] * 21
+    args[15] = ctypes.c_void_p(4100)                 # dw1 misaligned
+    st = lib.moe_expert_ffn_bwd(ctypes.byref(d), *args, p, need, None)
+    assert st == 1 and "dw1" in M.moe_last_error()
+    st = lib.moe_expert_ffn_bwd(ctypes.byref(d), *([p] * 21), p, need - 1, None)
+    assert st == 3
+    d2 = _dims(n_shared=1)                           # shared experts need dws2
+    args = [p] * 21
+    args[20] = None
+    st = lib.moe_expert_ffn_bwd(ctypes.byref(d2), *args, p, 1 << 30, None)
+    assert st == 1 and "dws2" in M.moe_last_error()
 
 
 def test_workspace_grows_with_tokens(lib):
