@@ -89,6 +89,26 @@ def kernel_stats(d: str):
     return rows
 
 
+def timed_means(d: str, skip: int):
+    """Per kernel: mean duration (us) of its dispatches after the first `skip`
+    (the warm-up steps), from the kernel trace; None where the trace is absent."""
+    try:
+        path = _one_csv(d, "kernel_trace.csv")
+    except FileNotFoundError:
+        return None
+    runs = defaultdict(list)
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            runs[short_name(r["Kernel_Name"])].append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    out = {}
+    for k, v in runs.items():
+        v.sort()
+        tail = [x[1] for x in v[skip:]] or [x[1] for x in v]
+        out[k] = sum(tail) / len(tail) / 1e3
+    return out
+
+
 def counter_means(d: str, counter: str):
     """Per kernel: mean counter value per dispatch (KiB for FETCH_SIZE / WRITE_SIZE)."""
     vals = defaultdict(list)
@@ -115,9 +135,19 @@ def cmd_stats(a):
            f"    {a.command}", ""]
     if a.note:
         out += [a.note, ""]
-    out += ["| kernel | calls | avg us | total ms | % |", "|---|---:|---:|---:|---:|"]
-    for n, c, avg, tot, pct in rows:
-        out.append(f"| {n} | {c} | {avg:.1f} | {tot:.2f} | {pct:.2f} |")
+    timed = timed_means(a.dir, a.skip) if a.skip else None
+    if timed is None:
+        out += ["| kernel | calls | avg us | total ms | % |", "|---|---:|---:|---:|---:|"]
+        for n, c, avg, tot, pct in rows:
+            out.append(f"| {n} | {c} | {avg:.1f} | {tot:.2f} | {pct:.2f} |")
+    else:
+        out += [f"avg us: all dispatches; timed avg us: without the first {a.skip} dispatches of "
+                "each kernel (the warm-up steps), the figure to set beside bench.py's per-call "
+                "event times.", ""]
+        out += ["| kernel | calls | avg us | timed avg us | total ms | % |",
+                "|---|---:|---:|---:|---:|---:|"]
+        for n, c, avg, tot, pct in rows:
+            out.append(f"| {n} | {c} | {avg:.1f} | {timed.get(n, avg):.1f} | {tot:.2f} | {pct:.2f} |")
     print("\n".join(out))
 
 
@@ -184,6 +214,7 @@ def main(argv=None):
     s.add_argument("--title", required=True)
     s.add_argument("--command", required=True)
     s.add_argument("--note", default="")
+    s.add_argument("--skip", type=int, default=0, help="warm-up dispatches per kernel to leave out")
     t = sp.add_parser("traffic")
     for n in ("fetch", "write", "copy-fetch", "copy-write", "workload", "out", "command-fetch",
               "command-write", "command-copy-fetch", "command-copy-write"):
