@@ -30,7 +30,7 @@ def _run(cfg, inp, fused=True, backward=True):
     b = L.Buffers(d, backward=backward)
     L.forward(b, p, fused=fused)
     if backward:
-        L.backward(b, p)
+        L.backward(b, p, fused=fused)
     torch.cuda.synchronize()
     return d, b
 
@@ -133,3 +133,26 @@ def test_full_size_reruns_bit_identical():
     _, b2 = _run(cfg, inp)
     for n in names:
         assert torch.equal(first[n], getattr(b2, n)), n
+
+
+@pytest.mark.parametrize("name", ["mixtral", "dsv3"])
+def test_full_size_one_launch_backward_bitwise(name):
+    """At the benchmarked sizes the one-launch backward gives the bits of the
+    plain B then W calls."""
+    cfg = synth.config(name)
+    print(f"case one-launch backward workload={name}", flush=True)
+    inp = synth.make_inputs(cfg, with_grad=True)
+    d = L.make_dims(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.n_shared, cfg.dtype)
+    p = {k: synth.to_torch(v, "cuda") for k, v in inp.items()}
+    b = L.Buffers(d)
+    L.forward(b, p, fused=True)
+    outs = ("dab", "dx_rows", "dw1", "dw3", "dw2", "dws1", "dws3", "dws2", "dx")
+    L.backward(b, p, fused=False)
+    torch.cuda.synchronize()
+    ref = {n: getattr(b, n).clone() for n in outs if getattr(b, n) is not None}
+    for n in ref:
+        getattr(b, n).fill_(7)
+    L.backward(b, p, fused=True)
+    torch.cuda.synchronize()
+    for n, t in ref.items():
+        assert torch.equal(t, getattr(b, n)), n
