@@ -14,8 +14,12 @@ Each library call inside the timed steps is bracketed by HIP events recorded
 on the stream the call launches on, so per-call device times are measured on
 the very steps that are timed.  The roofline entry is computed for the call
 with the largest total time from its algorithmic flop (or byte) count.
-The CPU baseline times the oracle (plain fp64 numpy) on a bounded sample of
-the same layer: the first --cpu-tokens tokens, full expert weights.
+After the timed steps one more step runs with a 512 MiB buffer written before
+every HBM-bound call, so that those calls read their inputs from HBM rather
+than from L2 or the 256 MiB Infinity Cache where the step leaves them;
+"hbm_flushed" reports their rates (the per-call figures are the unflushed
+ones).  The CPU baseline times the oracle (plain fp64 numpy) on a bounded
+sample of the same layer: the first --cpu-tokens tokens, full expert weights.
 """
 from __future__ import annotations
 
@@ -125,8 +129,13 @@ def main():
     fused = not args.unfused
 
     calls = []  # (name, start_event, end_event)
+    bpe = 2 if cfg.dtype == "bf16" else 4
+    work = algorithmic_work(d, bpe)
+    flush = {"buf": None}   # set: write it before every HBM-bound call (evicts L2 and MALL)
 
     def timed(name, fn, *a):
+        if flush["buf"] is not None and work[name][0] == "hbm":
+            flush["buf"].fill_(1)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -184,8 +193,23 @@ def main():
     for name, e0, e1 in calls:
         per_call.setdefault(name, []).append(e0.elapsed_time(e1))
     per_call_ms = {k: float(np.mean(v)) for k, v in per_call.items()}
-    bpe = 2 if cfg.dtype == "bf16" else 4
-    work = algorithmic_work(d, bpe)
+
+    # one more step, untimed as a whole: a 512 MiB buffer is written before
+    # each HBM-bound call, so its inputs come from HBM rather than from the
+    # 256 MiB Infinity Cache (MALL) or L2, where the step leaves them
+    calls.clear()
+    flush["buf"] = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    step()
+    torch.cuda.synchronize()
+    flush["buf"] = None
+    hbm_flushed = {}
+    for name, e0, e1 in calls:
+        kind, amount = work[name]
+        if kind == "hbm":
+            ms = e0.elapsed_time(e1)
+            rate = amount / (ms * 1e-3) / 1e9
+            hbm_flushed[name] = {"ms": round(ms, 4), "GB/s": round(rate, 1),
+                                 "frac": round(rate / PEAK_HBM_GBS, 4)}
     breakdown = {}
     for k, ms in per_call_ms.items():
         kind, amount = work[k]
@@ -233,6 +257,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_call": breakdown,
+        "hbm_flushed": hbm_flushed,
         "input_gen_s": round(gen_s, 1),
     }
     print(json.dumps(line), flush=True)

@@ -74,7 +74,8 @@ __global__ __launch_bounds__(kRowBlock) void combine_kernel(const S* __restrict_
 
 // dy[slot[t,k]] = w[t,k] dout[t];  dw[t,k] = <dout[t], y[slot[t,k]]>.
 // The dot product: per-lane partial sums in vector order, then a fixed
-// butterfly across the wave.
+// butterfly across the wave.  Each lane takes U vectors per round, so 2U
+// loads are in flight (the order of the partial sums is unchanged).
 template <typename S>
 __global__ __launch_bounds__(kRowBlock) void combine_bwd_kernel(const S* __restrict__ dout,
                                                                 const S* __restrict__ y,
@@ -84,6 +85,7 @@ __global__ __launch_bounds__(kRowBlock) void combine_bwd_kernel(const S* __restr
                                                                 float* __restrict__ dw, int T,
                                                                 int H, int K) {
   constexpr int P = Elem<S>::kPerVec;
+  constexpr int U = 8;
   const int t = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   if (t >= T) return;
@@ -92,60 +94,50 @@ __global__ __launch_bounds__(kRowBlock) void combine_bwd_kernel(const S* __restr
   const int nvec = H / P;
   const char* g_row = reinterpret_cast<const char*>(dout + (int64_t)t * H);
   for (int k = 0; k < K; ++k) {
-    const int s = __shfl(my_slot, k, kWave);
-    const float wk = __shfl(my_w, k, kWave);
+    const int s = lane_int(my_slot, k);
+    const float wk = lane_float(my_w, k);
     const char* y_row = reinterpret_cast<const char*>(y + (int64_t)s * H);
     char* dy_row = reinterpret_cast<char*>(dy + (int64_t)s * H);
     float part = 0.f;
-    for (int v = lane; v < nvec; v += kWave) {
-      float g[P], f[P], o[P];
-      Elem<S>::unpack(ld16(g_row + (int64_t)v * 16), g);
-      Elem<S>::unpack(ld16(y_row + (int64_t)v * 16), f);
+    for (int v0 = lane; v0 < nvec; v0 += kWave * U) {
+      u32x4 gr[U], yr[U];
 #pragma unroll
-      for (int j = 0; j < P; ++j) {
-        part = fmaf(g[j], f[j], part);
-        o[j] = wk * g[j];
+      for (int u = 0; u < U; ++u) {   // a lane past the row's end reloads its last vector
+        const int64_t v = min(v0 + u * kWave, nvec - 1);
+        gr[u] = ld16(g_row + v * 16);
+        yr[u] = ld16(y_row + v * 16);
       }
-      st16(dy_row + (int64_t)v * 16, Elem<S>::pack(o));
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * kWave;
+        if (v < nvec) {
+          float g[P], f[P], o[P];
+          Elem<S>::unpack(gr[u], g);
+          Elem<S>::unpack(yr[u], f);
+#pragma unroll
+          for (int jj = 0; jj < P; ++jj) {
+            part = fmaf(g[jj], f[jj], part);
+            o[jj] = wk * g[jj];
+          }
+          st16(dy_row + (int64_t)v * 16, Elem<S>::pack(o));
+        }
+      }
     }
     part = wave_sum(part);
     if (lane == 0) dw[(int64_t)t * K + k] = part;
   }
 }
 
-// dx[t] = sum_k dx_rows[slot[t,k]] + sum_s dx_rows[R + s*T + t]; one rounding.
+// dx[t] = sum_k dx_rows[slot[t,k]] + sum_s dx_rows[R + s*T + t]; one rounding
+// (the combine row with unit weights).
 template <typename S>
 __global__ __launch_bounds__(kRowBlock) void dispatch_bwd_kernel(const S* __restrict__ dx_rows,
                                                                  const int32_t* __restrict__ slot,
                                                                  S* __restrict__ dx, int T, int H,
                                                                  int K, int Ns) {
-  constexpr int P = Elem<S>::kPerVec;
   const int t = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
   if (t >= T) return;
-  const int my_slot = lane < K ? slot[(int64_t)t * K + lane] : 0;
-  const int64_t R = (int64_t)T * K;
-  const int nvec = H / P;
-  for (int v = lane; v < nvec; v += kWave) {
-    float acc[P];
-#pragma unroll
-    for (int j = 0; j < P; ++j) acc[j] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int s = lane_int(my_slot, k);
-      float f[P];
-      Elem<S>::unpack(ld16(reinterpret_cast<const char*>(dx_rows + (int64_t)s * H) + (int64_t)v * 16), f);
-#pragma unroll
-      for (int j = 0; j < P; ++j) acc[j] += f[j];
-    }
-    for (int sh = 0; sh < Ns; ++sh) {
-      float f[P];
-      Elem<S>::unpack(ld16(reinterpret_cast<const char*>(dx_rows + (R + (int64_t)sh * T + t) * H) +
-                           (int64_t)v * 16), f);
-#pragma unroll
-      for (int j = 0; j < P; ++j) acc[j] += f[j];
-    }
-    st16(reinterpret_cast<char*>(dx + (int64_t)t * H) + (int64_t)v * 16, Elem<S>::pack(acc));
-  }
+  combine_row<S>(dx_rows, slot, nullptr, dx, t, T, H, K, Ns, threadIdx.x & (kWave - 1));
 }
 
 // dl[t, e_k] = w_k (dw_k - sum_j w_j dw_j), zero for unselected experts.

@@ -9,15 +9,17 @@ namespace moe {
 // out[t] = sum_k w[t,k] y[slot[t,k]] + sum_s y[R + s*T + t]; one rounding.
 // Each lane takes U 16-byte column vectors per round (U loads of one row in
 // flight at a time); every element still sums k in ascending order, then the
-// shared rows, so the bits do not depend on U.
+// shared rows, so the bits do not depend on U.  w == nullptr: unit weights
+// (plain sums: the dispatch backward).
 template <typename S>
 __device__ __forceinline__ void combine_row(const S* __restrict__ y, const int32_t* __restrict__ slot,
                                             const float* __restrict__ w, S* __restrict__ out,
                                             int t, int T, int H, int K, int Ns, int lane) {
   constexpr int P = Elem<S>::kPerVec;
   constexpr int U = 8;
+  const bool weighted = w != nullptr;
   const int my_slot = lane < K ? slot[(int64_t)t * K + lane] : 0;
-  const float my_w = lane < K ? w[(int64_t)t * K + lane] : 0.f;
+  const float my_w = (weighted && lane < K) ? w[(int64_t)t * K + lane] : 0.f;
   const int64_t R = (int64_t)T * K;
   const int nvec = H / P;
   for (int v0 = lane; v0 < nvec; v0 += kWave * U) {
@@ -43,7 +45,7 @@ __device__ __forceinline__ void combine_row(const S* __restrict__ y, const int32
       for (int u = 0; u < U; ++u) {
         float f[P];
         Elem<S>::unpack(r[u], f);
-        if (k < K) {
+        if (k < K && weighted) {
 #pragma unroll
           for (int j = 0; j < P; ++j) acc[u][j] = fmaf(wk, f[j], acc[u][j]);
         } else {
