@@ -100,8 +100,8 @@ def main():
         copy_reference()
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the layer would shard by expert across GPUs, which is not built here)",
+        print(f"bench.py: the layer runs on one GPU; --gpus {args.gpus} is not supported "
+              "(across GPUs it would shard by expert, which is not implemented)",
               file=sys.stderr)
         sys.exit(2)
 
