@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--fwd-only", action="store_true")
+    ap.add_argument("--no-hbm-flush", action="store_true",
+                    help="skip the extra step that times the HBM-bound calls with the caches flushed")
     ap.add_argument("--route-ranks", type=int, default=0, metavar="G",
                     help="instead of the layer, time Algorithm 1 with G explicit ranks "
                          "(moe_route_ranks) on the workload's routing, beside the oracle")
@@ -198,11 +200,12 @@ def main():
     # each HBM-bound call, so its inputs come from HBM rather than from the
     # 256 MiB Infinity Cache (MALL) or L2, where the step leaves them
     calls.clear()
-    flush["buf"] = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    step()
-    torch.cuda.synchronize()
-    flush["buf"] = None
     hbm_flushed = {}
+    if not args.no_hbm_flush:
+        flush["buf"] = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        step()
+        torch.cuda.synchronize()
+        flush["buf"] = None
     for name, e0, e1 in calls:
         kind, amount = work[name]
         if kind == "hbm":
