@@ -83,3 +83,28 @@ def test_fused_reruns_bit_identical():
     for b in outs[1:]:
         for n in OUTS:
             assert torch.equal(getattr(outs[0], n), getattr(b, n)), n
+
+
+def test_dispatch_ffn_beyond_32_bit_row_offsets():
+    """x of 2 GiB: the fused kernel's per-lane byte offsets into x would not
+    fit 31 bits, so moe_dispatch_ffn runs the gather and the plain GEMM; the
+    result is still the unfused one."""
+    T, H, E, K, I = 131072, 8192, 2, 1, 64
+    print(f"case dispatch_ffn large x T={T} H={H}", flush=True)
+    assert T * H * 2 > 0x7FFF0000
+    g = torch.Generator(device="cuda").manual_seed(5)
+    p = {"logits": torch.randn(T, E, device="cuda", generator=g),
+         "x": torch.randn(T, H, device="cuda", generator=g).bfloat16(),
+         "w1": (0.02 * torch.randn(E, H, I, device="cuda", generator=g)).bfloat16(),
+         "w3": (0.02 * torch.randn(E, H, I, device="cuda", generator=g)).bfloat16(),
+         "w2": (0.02 * torch.randn(E, I, H, device="cuda", generator=g)).bfloat16()}
+    d = L.make_dims(T, H, E, K, I, 0, "bf16")
+    outs = {}
+    for fused in (False, True):
+        b = L.Buffers(d, backward=False)
+        L.forward(b, p, fused=fused)
+        torch.cuda.synchronize()
+        outs[fused] = {n: getattr(b, n).clone() for n in ("x_perm", "ab", "h", "out")}
+        del b
+    for n in outs[True]:
+        assert torch.equal(outs[False][n], outs[True][n]), n
