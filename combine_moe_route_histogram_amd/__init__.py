@@ -21,7 +21,7 @@ __all__ = [
     "moe_ffn_combine", "moe_combine_bwd", "moe_expert_ffn_bwd_data",
     "moe_expert_ffn_bwd_weight", "moe_dispatch_bwd", "moe_route_bwd", "moe_expert_ffn_bwd_act",
     "moe_expert_ffn_bwd_input", "moe_expert_ffn_bwd_weight_gate_up", "moe_expert_ffn_bwd_weight_down",
-    "moe_expert_ffn_bwd",
+    "moe_expert_ffn_bwd", "moe_sync_status",
 ]
 
 F32, BF16 = 0, 1
@@ -65,6 +65,7 @@ _SIGS = {
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_workspace_bytes": (ctypes.c_size_t, [_D]),
+    "moe_sync_status": (ctypes.c_int, [_P]),
     "moe_route": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_route_ranks_workspace_bytes": (ctypes.c_size_t, [_D, ctypes.c_int]),
     "moe_route_ranks": (ctypes.c_int, [_D, _P, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P,
@@ -125,6 +126,12 @@ def moe_init(device: int = 0) -> None:
     st = load().moe_init(device)
     if st:
         raise MoeError(st, "moe_init", moe_last_error())
+
+
+def moe_sync_status(stream=None) -> None:
+    """Wait for `stream`; raise MoeError (MOE_ETIMEOUT) if a bounded wait inside
+    a kernel gave up since the last check, or on a HIP error."""
+    _call("moe_sync_status", _stream(stream))
 
 
 def moe_workspace_bytes(d: Dims) -> int:

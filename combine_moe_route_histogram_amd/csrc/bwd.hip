@@ -95,7 +95,7 @@ void ffn_bwd_kernel(GemmArgs g, FusedWs w) {
   });
 
   // phases 3 and 4 read phase 1's output
-  wait_count(p1_done, n_mt * nt_bu);
+  wait_count(g, p1_done, n_mt * nt_bu);
 
   // phase 3: input gradient, tail split as in the plain launch
   for_tasks_xcd_ranges(cur + 2 * kXcds, n_mt * nt_bd, g.split_wr, (2 * g.I + BdCfg::BK - 1) / BdCfg::BK,
@@ -137,5 +137,7 @@ hipError_t launch_ffn_bwd(const GemmArgs& a0, const FusedWs& w, hipStream_t st) 
   ffn_bwd_kernel<<<w.workers, BuCfg::NT, 0, st>>>(a, w);
   return hipGetLastError();
 }
+
+hipError_t take_wait_error_bwd(uint32_t* out) { return take_wait_error(out); }
 
 }  // namespace moe

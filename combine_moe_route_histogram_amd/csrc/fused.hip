@@ -132,8 +132,7 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
         const int64_t row = q < g.K ? (int64_t)slot[(int64_t)t * g.K + q]
                                     : g.R + (int64_t)(q - g.K) * g.T + t;
         const int tile = tile_of_row(row, g, w.first_tile, C::BM);
-        while (__hip_atomic_load(&w.flags[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nt_count)
-          __builtin_amdgcn_s_sleep(2);
+        poll_at_least(g, &w.flags[tile], nt_count);
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
@@ -174,5 +173,7 @@ hipError_t launch_ffn_combine(const GemmArgs& a0, const int32_t* slot, const flo
   ffn_combine_kernel<<<w.workers, DownCfg::NT, 0, st>>>(a, slot, topk_w, w, nt);
   return hipGetLastError();
 }
+
+hipError_t take_wait_error_fused(uint32_t* out) { return take_wait_error(out); }
 
 }  // namespace moe

@@ -182,4 +182,6 @@ hipError_t launch_gemm(bool is_bf16, int kind, const GemmArgs& a, int4* mtiles_w
 #undef MOE_KIND
 }
 
+hipError_t take_wait_error_gemm(uint32_t* out) { return take_wait_error(out); }
+
 }  // namespace moe

@@ -704,17 +704,46 @@ __device__ __forceinline__ void publish_add(int32_t* counter) {
   __syncthreads();
 }
 
+// Record of a bounded wait that gave up: one word per code object (each
+// .hip file including this header has its own copy, taken by the host
+// through take_wait_error_*), set with a vector atomic.
+static __device__ uint32_t g_wait_error;
+
+// Poll until *counter >= n + g.wait_extra, giving up (and recording it) after
+// g.wait_ticks of the 100 MHz clock.  The caller's lanes may poll different
+// counters.
+__device__ __forceinline__ void poll_at_least(const GemmArgs& g, const int32_t* counter, int n) {
+  const int target = n + g.wait_extra;
+  if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return;
+  const uint64_t t0 = wall_clock64();
+  while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    if (wall_clock64() - t0 >= g.wait_ticks) {
+      __hip_atomic_fetch_or(&g_wait_error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
 // Wait until *counter >= n (thread 0 polls with relaxed loads), then one
 // agent-scope acquire in wave 0; the barrier orders the whole workgroup after
 // it.  (An acquiring load per poll would invalidate the L2 at every poll.)
-__device__ __forceinline__ void wait_count(const int32_t* counter, int n) {
+__device__ __forceinline__ void wait_count(const GemmArgs& g, const int32_t* counter, int n) {
   if (threadIdx.x < kWave) {
-    if (threadIdx.x == 0)
-      while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n)
-        __builtin_amdgcn_s_sleep(2);
+    if (threadIdx.x == 0) poll_at_least(g, counter, n);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
+}
+
+// Host: read and clear this code object's wait record.
+static inline hipError_t take_wait_error(uint32_t* out) {
+  hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_wait_error), sizeof(uint32_t), 0,
+                                     hipMemcpyDeviceToHost);
+  if (e != hipSuccess || *out == 0) return e;
+  const uint32_t zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_wait_error), &zero, sizeof(uint32_t), 0,
+                           hipMemcpyHostToDevice);
 }
 
 // The whole tile: a ring of LDS k slices filled by direct loads, MFMA over
@@ -894,7 +923,7 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
     if (part < parts - 1) {   // helper
       part_out = pbase + part * tile_floats;
     } else {                  // owner: wait for the helpers' partials
-      wait_count(cnt, parts - 1);
+      wait_count(g, cnt, parts - 1);
       part_in = pbase;
       n_in = parts - 1;
     }

@@ -88,7 +88,17 @@ struct GemmArgs {
   float* split_part;       // [kXcds * kSplitSlots] partial tiles of BM x BN f32
   int32_t* split_cnt;      // [kXcds * kSplitWr] finished helper parts per split tile
   int split_wr;            // nominal workers per XCD (0: no split)
+  // bounded in-kernel waits: give up after wait_ticks of the 100 MHz clock;
+  // wait_extra (debug, 0 or 1) is added to every wait's target
+  uint64_t wait_ticks;
+  int wait_extra;
 };
+
+// Bounded-wait records, one error word per code object (.hip file): take
+// (read and clear) the word of each.
+hipError_t take_wait_error_gemm(uint32_t* out);
+hipError_t take_wait_error_fused(uint32_t* out);
+hipError_t take_wait_error_bwd(uint32_t* out);
 
 // Tail split constants: kSplitWr nominal workers per XCD (256 CUs / 8 XCDs
 // on MI355X; a plan constant, so results do not depend on how many workers

@@ -110,8 +110,24 @@ int check_ws(const moe_dims* d, const void* ws, size_t ws_bytes) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Bound of the in-kernel waits, in ticks of the 100 MHz clock: 20 s, or
+// MOE_WAIT_LIMIT_US microseconds; MOE_DEBUG_UNREACHABLE_WAITS=1 adds one to
+// every wait's target (debug: exercises the timeout record).  Read at every
+// launch.
+void wait_bounds(GemmArgs& a) {
+  a.wait_ticks = 20ull * 100000000ull;
+  if (const char* e = getenv("MOE_WAIT_LIMIT_US")) {
+    char* end = nullptr;
+    const unsigned long long us = strtoull(e, &end, 10);
+    if (end != e) a.wait_ticks = us * 100ull;
+  }
+  const char* u = getenv("MOE_DEBUG_UNREACHABLE_WAITS");
+  a.wait_extra = (u && u[0] == '1') ? 1 : 0;
+}
+
 GemmArgs base_args(const moe_dims* d, const int32_t* offsets, void* ws) {
   GemmArgs a{};
+  wait_bounds(a);
   a.T = d->T; a.H = d->H; a.E = d->E; a.K = d->K; a.I = d->I; a.Ns = d->n_shared;
   a.R = d->T * d->K;
   a.offsets = offsets;
@@ -205,6 +221,7 @@ const char* moe_status_str(int status) {
     case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED";
     case MOE_EWORKSPACE: return "MOE_EWORKSPACE";
     case MOE_EHIP: return "MOE_EHIP";
+    case MOE_ETIMEOUT: return "MOE_ETIMEOUT";
     default: return "MOE_UNKNOWN";
   }
 }
@@ -553,6 +570,20 @@ int moe_expert_ffn_bwd(const moe_dims* d, const void* dy, const void* dout,
   FusedWs w;
   MOE_TRY(fused_ws(d, ws, &w));
   return hip_status(launch_ffn_bwd(a, w, as_stream(stream)), "moe_expert_ffn_bwd");
+}
+
+int moe_sync_status(void* stream) {
+  MOE_TRY(hip_status(hipStreamSynchronize(as_stream(stream)), "moe_sync_status"));
+  uint32_t any = 0;
+  hipError_t (*const take[])(uint32_t*) = {take_wait_error_gemm, take_wait_error_fused,
+                                           take_wait_error_bwd};
+  for (auto f : take) {
+    uint32_t v = 0;
+    MOE_TRY(hip_status(f(&v), "moe_sync_status"));
+    any |= v;
+  }
+  if (any) return fail(MOE_ETIMEOUT, "a bounded wait inside a kernel gave up; results are invalid");
+  return MOE_OK;
 }
 
 int moe_dispatch_bwd(const moe_dims* d, const void* dx_rows, const int32_t* slot, void* dx,

@@ -58,7 +58,8 @@ typedef enum {
   MOE_EINVAL = 1,       /* bad argument (null pointer, bad shape)            */
   MOE_EUNSUPPORTED = 2, /* shape/dtype outside what the kernels support       */
   MOE_EWORKSPACE = 3,   /* workspace missing or smaller than moe_workspace_bytes */
-  MOE_EHIP = 4          /* a HIP runtime call failed (see moe_last_error)     */
+  MOE_EHIP = 4,         /* a HIP runtime call failed (see moe_last_error)     */
+  MOE_ETIMEOUT = 5      /* a bounded wait inside a kernel gave up (moe_sync_status) */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -82,6 +83,19 @@ const char* moe_status_str(int status);
 
 /* Detail of the last error returned on this thread ("" if none). */
 const char* moe_last_error(void);
+
+/* Synchronises `stream` (the host waits for its work) and reports what the
+ * kernels recorded while running.  The persistent kernels' waits (combine
+ * tasks on their row tiles, split-tail owners on their helpers, the
+ * one-launch backward on its first phase) always end by construction; each
+ * is also bounded in time (20 s, or MOE_WAIT_LIMIT_US microseconds from the
+ * environment, read at launch), and one that gives up records it on the
+ * device and lets the kernel run to its end with invalid results.
+ * Returns MOE_ETIMEOUT if any wait gave up since the last call (then clears
+ * the record), MOE_EHIP if the stream reports a HIP error, MOE_OK otherwise.
+ * Debug: MOE_DEBUG_UNREACHABLE_WAITS=1 in the environment at launch makes
+ * every such wait target one more than can happen, to exercise this path. */
+int moe_sync_status(void* stream);
 
 /* Bytes of device workspace the calls that take `ws` need for these dims
  * (route scratch, tile tables, readiness flags, task cursors).  The same

@@ -59,6 +59,7 @@ def test_binding_signatures_match_header():
 def test_status_strings(lib):
     assert M.moe_status_str(0) == "MOE_OK"
     assert M.moe_status_str(3) == "MOE_EWORKSPACE"
+    assert M.moe_status_str(5) == "MOE_ETIMEOUT"
     assert M.moe_status_str(99) == "MOE_UNKNOWN"
 
 
