@@ -53,6 +53,7 @@ static_assert(BuCfg::STAGE_BYTES == BdCfg::STAGE_BYTES && BuCfg::STAGE_BYTES == 
               "one LDS ring for every phase");
 static_assert(BuCfg::BM == BdCfg::BM, "both data-gradient phases use one row-tile table");
 
+template <bool R>
 __global__ __launch_bounds__(BuCfg::NT) __attribute__((amdgpu_waves_per_eu(BuCfg::NW / 4, BuCfg::NW / 4)))
 void ffn_bwd_kernel(GemmArgs g, FusedWs w) {
   MOE_LDS_RING(BuCfg, ring);
@@ -73,7 +74,7 @@ void ffn_bwd_kernel(GemmArgs g, FusedWs w) {
     int tm, tn;
     band_order_groups(tp.L, nt_bu, g.bands, g.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kBwdUp, BuCfg::BM, BuCfg::BN>(g, tm, tn);
-    if (!d.skip) run_tile_bf16<BuCfg>(g, d, ring, tp);
+    if (!d.skip) run_tile_bf16<BuCfg, false, R>(g, d, ring, tp);
     ++mine;
   });
   // publish this worker's phase-1 rows: own stores complete, one release,
@@ -91,7 +92,7 @@ void ffn_bwd_kernel(GemmArgs g, FusedWs w) {
     int tm, tn;
     band_order(tp.L, mt_wd, nt_wd, tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kWgDown, WdCfg::BM, WdCfg::BN>(g, tm, tn);
-    if (!d.skip) run_tile_bf16<WdCfg>(g, d, ring, tp);
+    if (!d.skip) run_tile_bf16<WdCfg, false, R>(g, d, ring, tp);
   });
 
   // phases 3 and 4 read phase 1's output
@@ -103,7 +104,7 @@ void ffn_bwd_kernel(GemmArgs g, FusedWs w) {
     int tm, tn;
     band_order_groups(tp.L, nt_bd, g.bands, g.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kBwdDown, BdCfg::BM, BdCfg::BN>(g, tm, tn);
-    if (!d.skip) run_tile_bf16<BdCfg>(g, d, ring, tp);
+    if (!d.skip) run_tile_bf16<BdCfg, false, R>(g, d, ring, tp);
   });
 
   // phase 4: dW1 | dW3
@@ -111,7 +112,7 @@ void ffn_bwd_kernel(GemmArgs g, FusedWs w) {
     int tm, tn;
     band_order(tp.L, mt_wu, nt_wu, tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kWgUp, WuCfg::BM, WuCfg::BN>(g, tm, tn);
-    if (!d.skip) run_tile_bf16<WuCfg>(g, d, ring, tp);
+    if (!d.skip) run_tile_bf16<WuCfg, false, R>(g, d, ring, tp);
   });
 }
 
@@ -134,7 +135,10 @@ hipError_t launch_ffn_bwd(const GemmArgs& a0, const FusedWs& w, hipStream_t st) 
                         (int64_t)(a.E + a.Ns) * wgrad_mtiles<kWgUp>(a.H, a.I, WuCfg::BM) *
                             gemm_ntiles<kWgUp>(a.H, a.I, WuCfg::BN);
   if (tiles > INT_MAX - 8) return hipErrorInvalidValue;
-  ffn_bwd_kernel<<<w.workers, BuCfg::NT, 0, st>>>(a, w);
+  if (ragged_k(a.H, a.I, BuCfg::BK))
+    ffn_bwd_kernel<true><<<w.workers, BuCfg::NT, 0, st>>>(a, w);
+  else
+    ffn_bwd_kernel<false><<<w.workers, BuCfg::NT, 0, st>>>(a, w);
   return hipGetLastError();
 }
 

@@ -43,6 +43,7 @@ namespace moe {
 using UpCfg = BfPick<kUp>::C;
 using DownCfg = BfPick<kDown>::C;
 
+template <bool R>
 __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
                                                                   const int32_t* __restrict__ slot_src,
                                                                   FusedWs w, int nt_count) {
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
     int tm, tn;
     band_order_groups(tp.L, nt_count, w.bands, w.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kUp, C::BM, C::BN>(g, tm, tn);
-    run_tile_bf16<C>(g, d, ring, tp);
+    run_tile_bf16<C, false, R>(g, d, ring, tp);
   });
   // phase 2: the permuted copy x_perm (an output the backward reads), one
   // row tile per task, filling the workers that the tile tail leaves idle
@@ -98,6 +99,7 @@ __device__ __forceinline__ int tile_of_row(int64_t row, const GemmArgs& g, const
 
 constexpr int kCombineTokens = 16;  // tokens per combine task
 
+template <bool R>
 __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
                                                                    const int32_t* __restrict__ slot,
                                                                    const float* __restrict__ topk_w,
@@ -114,7 +116,7 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
     int tm, tn;
     band_order_groups(tp.L, nt_count, w.bands, w.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kDown, C::BM, C::BN>(g, tm, tn);
-    run_tile_bf16<C, true>(g, d, ring, tp);
+    run_tile_bf16<C, true, R>(g, d, ring, tp);
     if (tp.part == tp.parts - 1) publish_add(&w.flags[tm]);   // the tile is complete
   });
   // phase 2: combine tasks, each token once all its rows' tiles are done
@@ -155,7 +157,10 @@ hipError_t launch_dispatch_ffn(const GemmArgs& a0, const int32_t* slot_src, cons
                              w.mt_bound + kFusedCursors + kXcds * kSplitWr, st);
   if (e != hipSuccess) return e;
   const int nt = gemm_ntiles<kUp>(a.H, a.I, UpCfg::BN);
-  dispatch_ffn_kernel<<<w.workers, UpCfg::NT, 0, st>>>(a, slot_src, w, nt);
+  if (ragged_k(a.H, a.I, UpCfg::BK))
+    dispatch_ffn_kernel<true><<<w.workers, UpCfg::NT, 0, st>>>(a, slot_src, w, nt);
+  else
+    dispatch_ffn_kernel<false><<<w.workers, UpCfg::NT, 0, st>>>(a, slot_src, w, nt);
   return hipGetLastError();
 }
 
@@ -170,7 +175,10 @@ hipError_t launch_ffn_combine(const GemmArgs& a0, const int32_t* slot, const flo
                              w.mt_bound + kFusedCursors + kXcds * kSplitWr, st);
   if (e != hipSuccess) return e;
   const int nt = gemm_ntiles<kDown>(a.H, a.I, DownCfg::BN);
-  ffn_combine_kernel<<<w.workers, DownCfg::NT, 0, st>>>(a, slot, topk_w, w, nt);
+  if (ragged_k(a.H, a.I, DownCfg::BK))
+    ffn_combine_kernel<true><<<w.workers, DownCfg::NT, 0, st>>>(a, slot, topk_w, w, nt);
+  else
+    ffn_combine_kernel<false><<<w.workers, DownCfg::NT, 0, st>>>(a, slot, topk_w, w, nt);
   return hipGetLastError();
 }
 

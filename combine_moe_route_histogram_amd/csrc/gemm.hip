@@ -96,7 +96,7 @@ inline int64_t kind_k_len(const GemmArgs& a) {
 // Persistent workers over per-XCD tile ranges (see for_tasks_xcd_ranges).
 // Forward kinds read the number of row tiles from the planner's device output,
 // so the tile count is exact; weight-gradient kinds have a fixed tile grid.
-template <class C>
+template <class C, bool R>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
 void gemm_bf16_kernel(GemmArgs g, int mt_fixed, int nt_count, int32_t* cursors, int max_parts) {
   MOE_LDS_RING(C, ring);
@@ -110,7 +110,7 @@ void gemm_bf16_kernel(GemmArgs g, int mt_fixed, int nt_count, int32_t* cursors, 
     else
       band_order_groups(tp.L, nt_count, g.bands, g.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, C::KIND, C::BM, C::BN>(g, tm, tn);
-    if (!d.skip) run_tile_bf16<C>(g, d, ring, tp);
+    if (!d.skip) run_tile_bf16<C, false, R>(g, d, ring, tp);
   });
 }
 
@@ -159,7 +159,11 @@ static hipError_t launch_kind(bool is_bf16, GemmArgs a, int4* mtiles_ws, int32_t
   if (is_bf16) {
     const int grid = (int)std::min<int64_t>(tiles * kMaxSplit, workers);
     const int max_parts = (int)((kind_k_len<KIND>(a) + C::BK - 1) / C::BK);
-    gemm_bf16_kernel<C><<<grid, C::NT, 0, st>>>(a, mt_count, nt_count, cursors, max_parts);
+    // H or I not a whole number of k slices: the instantiation with ragged k
+    if (ragged_k(a.H, a.I, C::BK))
+      gemm_bf16_kernel<C, true><<<grid, C::NT, 0, st>>>(a, mt_count, nt_count, cursors, max_parts);
+    else
+      gemm_bf16_kernel<C, false><<<grid, C::NT, 0, st>>>(a, mt_count, nt_count, cursors, max_parts);
   } else {
     gemm_f32_kernel<KIND><<<(int)tiles, kF32NT, 0, st>>>(a, mt_count, nt_count);
   }

@@ -303,7 +303,8 @@ struct DmaOperand {
   static_assert(!MN || kHMN >= 128, "MN sub-tiles need >= 128 columns");
   static_assert(MN || NH == 1, "KC operands have one source");
   uint32_t off[kPerWave];   // per-lane byte offset (relative to the k slice start) or invalid
-  int krow[RAGGED_K ? kPerWave : 1];  // MN with ragged K: k row of this lane
+  int krow[RAGGED_K ? kPerWave : 1];  // ragged K: k of this lane's load within the slice
+                                      // (MN: its k row; KC: its chunk's first k)
   // s = row stride (KC) or k stride (MN) in elements; mn_valid per sub-tile;
   // rows (KC only, may be null): source row of each tile row, for gathered
   // operands (the host keeps every such byte offset below 2^31).
@@ -322,6 +323,7 @@ struct DmaOperand {
         } else {
           off[i] = kBufInvalid;
         }
+        if constexpr (RAGGED_K) krow[i] = c * 8;
       } else {
         constexpr int kQHalf = kHMN * BK * 2 / 1024;         // instructions per sub-tile
         const int qh = q % kQHalf;
@@ -335,8 +337,9 @@ struct DmaOperand {
     }
   }
   // Issue the copy of one k slice.  src0/src1: operand at (k slice start,
-  // column 0) of sub-tile 0/1 (KC: row 0 at k0); k_valid: valid k rows (MN);
-  // live false: the slice lies past the end of k and is filled with zeros.
+  // column 0) of sub-tile 0/1 (KC: row 0 at k0); k_valid: valid k of the
+  // slice (used with RAGGED_K; loads past it are zero-filled); live false:
+  // the slice lies past the end of k and is filled with zeros.
   __device__ __forceinline__ void issue(uint8_t* stage, const uint16_t* src0, const uint16_t* src1,
                                         int k_valid, bool live, int wave) const {
 #pragma unroll
@@ -349,7 +352,7 @@ struct DmaOperand {
       }
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(src);
       uint32_t o = live ? off[i] : kBufInvalid;
-      if constexpr (MN && RAGGED_K) o = krow[i] < k_valid ? o : kBufInvalid;
+      if constexpr (RAGGED_K) o = krow[i] < k_valid ? o : kBufInvalid;
       dma16(rs, stage + q * 1024, o);
     }
   }
@@ -746,13 +749,18 @@ static inline hipError_t take_wait_error(uint32_t* out) {
                            hipMemcpyHostToDevice);
 }
 
+// H or I is not a whole number of k slices (both are multiples of 8): the
+// forward-shaped kinds then run the instantiation that zero-fills past the
+// end of k.
+inline bool ragged_k(int H, int I, int bk) { return (H % bk) != 0 || (I % bk) != 0; }
+
 // The whole tile: a ring of LDS k slices filled by direct loads, MFMA over
 // each slice with the next k step's fragments in flight, then the epilogue.
 // A split tile's helper part stores its partial sums and publishes them; the
 // owner part (the last) waits for its helpers, adds their partials in part
 // order (a fixed order, so the bits do not depend on timing) and runs the
 // epilogue.
-template <class C, bool kCoherentY = false>
+template <class C, bool kCoherentY = false, bool kRaggedK = false>
 __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
                               uint8_t* const (&stages)[4], const TaskPart& tp) {
   constexpr int MI = C::MI, NJ = C::NJ;
@@ -762,9 +770,9 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / C::WGN, wn = wave % C::WGN;
 
-  // only the weight gradient has a k range (an expert's rows) that is not a
-  // whole number of slices
-  constexpr bool kRagged = KindTraits<C::KIND>::kWgrad;
+  // the weight gradient's k range (an expert's rows) is not a whole number
+  // of slices; kRaggedK: neither is H or I (multiples of 8, not of the slice)
+  constexpr bool kRagged = KindTraits<C::KIND>::kWgrad || kRaggedK;
   DmaOperand<C::BM, C::NW, C::A_MN, 1, kRagged, C::BK> da;
   DmaOperand<C::BN, C::NW, C::B_MN, C::B_NH, kRagged, C::BK> db;
   if constexpr (C::A_MN) da.init(d.a_sk, d.m_valid, wave, lane); else da.init(d.a_sm, d.m_valid, wave, lane, d.a_rows);
@@ -774,22 +782,32 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
   constexpr bool kSplit = KindTraits<C::KIND>::kSplit;
   const int parts = kSplit ? tp.parts : 1;
   const int part = kSplit ? tp.part : 0;
-  const int nk_all = (d.k_len + BK - 1) / BK;
+  // The input gradient's k runs over [da | db] against [W1 | W3]: two
+  // segments of ksplit = I each, every segment a whole number of slices (the
+  // last slice of a segment partial when I is not a multiple of BK).
+  const bool two_seg = d.ksplit != INT_MAX;
+  const int nk_seg = two_seg ? (d.ksplit + BK - 1) / BK : 0;
+  const int nk_all = two_seg ? 2 * nk_seg : (d.k_len + BK - 1) / BK;
   const int kb = parts > 1 ? (int)((int64_t)nk_all * part / parts) : 0;   // this part's slices
   const int nk = parts > 1 ? (int)((int64_t)nk_all * (part + 1) / parts) - kb : nk_all;
   auto issue = [&](uint8_t* st, int kt) {   // kt: slice index within the part
-    const int k0 = (kb + kt) * BK;
+    int ks = (kb + kt) * BK;                 // k of the slice within its segment
+    int seg = 0;
+    if (two_seg && kb + kt >= nk_seg) {
+      seg = 1;
+      ks -= nk_seg * BK;
+    }
+    const int k_valid = (two_seg ? d.ksplit : d.k_len) - ks;
     const bool live = kt < nk;   // kt < nk_pad always; zero-filled past nk
     if constexpr (C::A_MN)
-      da.issue(st, d.a + (int64_t)k0 * d.a_sk, nullptr, d.k_len - k0, live, wave);
+      da.issue(st, d.a + (int64_t)ks * d.a_sk, nullptr, k_valid, live, wave);
     else
-      da.issue(st, d.a + k0, nullptr, 0, live, wave);
+      da.issue(st, d.a + (seg ? d.ksplit : 0) + ks, nullptr, k_valid, live, wave);
     if constexpr (C::B_MN)
-      db.issue(st + C::A_BYTES, d.b0 + (int64_t)k0 * d.b_sk,
-               C::PAIRED ? d.b1 + (int64_t)k0 * d.b_sk : nullptr, d.k_len - k0, live, wave);
+      db.issue(st + C::A_BYTES, d.b0 + (int64_t)ks * d.b_sk,
+               C::PAIRED ? d.b1 + (int64_t)ks * d.b_sk : nullptr, k_valid, live, wave);
     else
-      db.issue(st + C::A_BYTES, k0 < d.ksplit ? d.b0 + k0 : d.b1 + (k0 - d.ksplit), nullptr, 0, live,
-               wave);
+      db.issue(st + C::A_BYTES, (seg ? d.b1 : d.b0) + ks, nullptr, k_valid, live, wave);
   };
 
   f32x16 acc[MI][NJ];

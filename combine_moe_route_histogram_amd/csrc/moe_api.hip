@@ -74,10 +74,10 @@ int check_dims(const moe_dims* d) {
   if (d->E < 1 || d->E > 256) return fail(MOE_EUNSUPPORTED, "E must be in [1, 256] (got %d)", d->E);
   if (d->K < 1 || d->K > d->E || d->K > 64)
     return fail(MOE_EUNSUPPORTED, "K must be in [1, min(E, 64)] (got K=%d, E=%d)", d->K, d->E);
-  if (d->H <= 0 || d->H % 64)
-    return fail(MOE_EUNSUPPORTED, "H must be a positive multiple of 64 (got %d)", d->H);
-  if (d->I <= 0 || d->I % 64)
-    return fail(MOE_EUNSUPPORTED, "I must be a positive multiple of 64 (got %d)", d->I);
+  if (d->H <= 0 || d->H % 8)
+    return fail(MOE_EUNSUPPORTED, "H must be a positive multiple of 8 (got %d)", d->H);
+  if (d->I <= 0 || d->I % 8)
+    return fail(MOE_EUNSUPPORTED, "I must be a positive multiple of 8 (got %d)", d->I);
   if (d->n_shared < 0 || d->n_shared > 8)
     return fail(MOE_EUNSUPPORTED, "n_shared must be in [0, 8] (got %d)", d->n_shared);
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16)

@@ -38,7 +38,7 @@
  *  - Every call returns a moe_status.  On error nothing has been launched
  *    and moe_last_error() gives a message (thread-local).
  *  - Validation (else MOE_EINVAL / MOE_EUNSUPPORTED): T >= 1,
- *    1 <= K <= E <= 256, K <= 64, H and I positive multiples of 64,
+ *    1 <= K <= E <= 256, K <= 64, H and I positive multiples of 8,
  *    0 <= Ns <= 8, R + Ns*T < 2^31; non-null pointers for every buffer the
  *    call uses.  Element offsets are computed in 64 bits, so buffers larger
  *    than 2^31 elements are fine.

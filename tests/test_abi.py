@@ -71,7 +71,7 @@ def _dims(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(T=0), 1), (dict(E=0), 2), (dict(E=257), 2), (dict(K=0), 2), (dict(K=9), 2),
-    (dict(E=128, K=65), 2), (dict(H=100), 2), (dict(I=96), 2), (dict(n_shared=9), 2),
+    (dict(E=128, K=65), 2), (dict(H=100), 2), (dict(I=100), 2), (dict(n_shared=9), 2),
     (dict(dtype=5), 2),
 ])
 def test_bad_dims_rejected_without_launch(lib, kw, status):

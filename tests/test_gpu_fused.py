@@ -22,6 +22,7 @@ SHAPES = [
     (520, 192, 16, 4, 128, 0),
     (64, 128, 1, 1, 128, 1),
     (96, 64, 24, 12, 64, 1),      # 13 rows per token: the combine polls many tiles
+    (200, 200, 6, 2, 136, 0),     # H, I not whole k slices
 ]
 OUTS = ("x_perm", "ab", "h", "y", "out")
 

@@ -22,6 +22,7 @@ SHAPES = [
     (520, 192, 16, 4, 128, 0),    # empty and huge experts
     (64, 128, 1, 1, 128, 1),      # one expert, one row tile
     (1, 64, 4, 2, 64, 0),         # a single token: most experts empty
+    (150, 72, 4, 2, 88, 1),       # H, I not whole k slices, a shared expert
 ]
 OUTS = ("dab", "dx_rows", "dw1", "dw3", "dw2", "dws1", "dws3", "dws2", "dx", "dtopk_w", "dlogits")
 

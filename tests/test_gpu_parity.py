@@ -27,6 +27,8 @@ SHAPES = [
     (1, 128, 4, 2, 128, 0),       # a single token
     (520, 192, 16, 4, 128, 0),    # skewed: empty and huge experts (see logits below)
     (96, 64, 32, 20, 64, 1),      # more rows per token than 16-byte vectors per row
+    (200, 200, 6, 2, 136, 0),     # H, I multiples of 8, not of the 64-wide k slice
+    (150, 72, 4, 2, 88, 1),       # the same with a shared expert
 ]
 
 
