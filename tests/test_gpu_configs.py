@@ -8,7 +8,9 @@ seeded sample of permuted rows (bit-exact); a seeded sample of tokens whose
 outputs, input gradients and gate gradients the oracle evaluates one by one
 from the definition (normwise max-rel-err <= 2e-2 for bf16, max-abs-err <=
 1e-5 for the fp32 workload); a seeded sample of intermediate units whose
-columns of dW1/dW3 and rows of dW2 the oracle forms for sampled experts.
+columns of dW1/dW3 and rows of dW2 the oracle forms for sampled experts, and
+the weight gradients of whole experts (two at the long-sequence size, where
+the token sample is 4096, one elsewhere).
 """
 import numpy as np
 import pytest
@@ -66,7 +68,8 @@ def test_full_size_workload(name):
     assert np.array_equal(_rows(b.x_perm, ss), inp["x"][slot_src[ss]])
 
     # token outputs from the definition
-    toks = np.sort(rng.choice(T, size=12, replace=False))
+    # 4096 sampled tokens at the long-sequence size, 256 elsewhere
+    toks = np.sort(rng.choice(T, size=4096 if name == "longseq" else 256, replace=False))
     out_ref, _ = O.tokens_forward(inp["x"][toks], idx[toks], w[toks], inp, dt)
     assert max_rel(_rows(b.out, toks), out_ref, dt) <= BF16_TOL
 
@@ -79,7 +82,7 @@ def test_full_size_workload(name):
     assert f32_rel(_rows(b.dlogits, toks), dl_ref) <= BF16_TOL
 
     # weight-gradient columns of sampled experts and intermediate units
-    cols = np.sort(rng.choice(cfg.I, size=3, replace=False))
+    cols = np.sort(rng.choice(cfg.I, size=8, replace=False))
     experts = np.sort(rng.choice(np.nonzero(counts)[0], size=min(3, int((counts > 0).sum())), replace=False))
     g64 = O.widen(inp["dout"], dt)
     for e in experts:
@@ -93,6 +96,19 @@ def test_full_size_workload(name):
         assert f32_rel(host(b.dw1[e_t][:, torch.as_tensor(cols)]), d1) <= BF16_TOL
         assert f32_rel(host(b.dw3[e_t][:, torch.as_tensor(cols)]), d3) <= BF16_TOL
         assert f32_rel(host(b.dw2[e_t][torch.as_tensor(cols)]), d2) <= BF16_TOL
+    # whole routed experts' weight gradients: two at the long-sequence size, one elsewhere
+    for e in experts[: 2 if name == "longseq" else 1]:
+        e = int(e)
+        rows = np.arange(offsets[e], offsets[e + 1])
+        toks_e = slot_src[rows]
+        k_e = np.argmax(idx[toks_e] == e, axis=1)
+        DY = O.store(w[toks_e, k_e].astype(np.float64)[:, None] * g64[toks_e], dt)
+        d1, d3, d2 = O.expert_wgrad_columns(inp["x"][toks_e], DY, inp["w1"][e], inp["w3"][e],
+                                            inp["w2"][e], np.arange(cfg.I), dt)
+        e_t = torch.tensor(e)
+        assert f32_rel(host(b.dw1[e_t]), d1) <= BF16_TOL
+        assert f32_rel(host(b.dw3[e_t]), d3) <= BF16_TOL
+        assert f32_rel(host(b.dw2[e_t]), d2) <= BF16_TOL
     for s in range(cfg.n_shared):
         sub = {"w1": inp["ws1"], "w3": inp["ws3"], "w2": inp["ws2"]}
         d1, d3, d2 = O.expert_wgrad_columns(inp["x"], inp["dout"], sub["w1"][s], sub["w3"][s],
