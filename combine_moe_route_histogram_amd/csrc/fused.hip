@@ -26,10 +26,13 @@
 // from the others.  Tiles that share weight columns and token rows then run
 // on one XCD and share its L2, as in the plain launch.
 //
-// Deadlock freedom: only combine tasks wait, and only on GEMM tiles; a worker
-// takes combine tasks only once every tile has been claimed, by a worker that
-// is running and never waits, so every wait ends, whatever the number of
-// resident workers.
+// Deadlock freedom: combine tasks wait on GEMM tiles, and the owner of a
+// split tail tile waits on its helper parts.  A worker takes combine tasks
+// only once every tile has been claimed, and a split tile's helpers are
+// claimed before its owner; helpers and whole tiles never wait, so every wait
+// is on work that a running worker has already claimed and will finish,
+// whatever the number of resident workers.  (Each wait is also bounded in
+// time; one that gives up is recorded for moe_sync_status.)
 //
 // Determinism: every GEMM tile runs the same tile code with the same operands
 // as the plain launch and every combine row the same combine code, so the
