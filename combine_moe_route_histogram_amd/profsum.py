@@ -51,8 +51,17 @@ CALL_KERNEL = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments and blank space (a comment edit does not
+    change the kernels)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_fingerprint() -> str:
-    """sha256 over the kernel sources, the public header and the build flags."""
+    """sha256 over the code of the kernel sources and the public header
+    (comments and blank space left out) and the build flags."""
     from . import build as B
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")) +
@@ -60,8 +69,8 @@ def source_fingerprint() -> str:
                    glob.glob(os.path.join(ROOT, "include", "*.h")))
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     h.update(" ".join(B.COMMON_FLAGS[1:]).replace(ROOT, "").encode())
     return h.hexdigest()[:16]
 
