@@ -93,6 +93,8 @@ const char* moe_last_error(void);
  * device and lets the kernel run to its end with invalid results.
  * Returns MOE_ETIMEOUT if any wait gave up since the last call (then clears
  * the record), MOE_EHIP if the stream reports a HIP error, MOE_OK otherwise.
+ * The record is kept per device (the current one), not per stream: a wait
+ * that gave up in work on another stream of the device is reported too.
  * Debug: MOE_DEBUG_UNREACHABLE_WAITS=1 in the environment at launch makes
  * every such wait target one more than can happen, to exercise this path. */
 int moe_sync_status(void* stream);

@@ -56,6 +56,21 @@ def test_binding_signatures_match_header():
         assert len(M._SIGS[name][1]) == n, (name, len(M._SIGS[name][1]), n)
 
 
+@pytest.mark.parametrize("lang", ["c", "c++"])
+def test_header_compiles_standalone(lang, tmp_path):
+    """include/moe.h is a plain C header: it compiles on its own as C and C++."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("no host compiler")
+    src = tmp_path / ("t.c" if lang == "c" else "t.cpp")
+    src.write_text('#include "moe.h"\nint main(void) { moe_dims d = {0}; return (int)sizeof(d) - 28; }\n')
+    r = subprocess.run([cc, "-Wall", "-Werror", "-fsyntax-only", "-I", os.path.dirname(HEADER), str(src)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_status_strings(lib):
     assert M.moe_status_str(0) == "MOE_OK"
     assert M.moe_status_str(3) == "MOE_EWORKSPACE"
