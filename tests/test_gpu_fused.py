@@ -23,6 +23,8 @@ SHAPES = [
     (64, 128, 1, 1, 128, 1),
     (96, 64, 24, 12, 64, 1),      # 13 rows per token: the combine polls many tiles
     (200, 200, 6, 2, 136, 0),     # H, I not whole k slices
+    (64, 64, 4, 4, 64, 0),        # K = E: every expert holds every token
+    (40, 128, 256, 8, 64, 0),     # 256 experts, most of them empty
 ]
 OUTS = ("x_perm", "ab", "h", "y", "out")
 
