@@ -54,7 +54,6 @@ __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
   MOE_LDS_RING(C, ring);
   __shared__ int task_slot;
   const int n_mt = *w.n_mtiles;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int nvec = g.H / 8;
   // phase 1: GEMM tiles; the routed rows' A operand is gathered from the token
   // rows as it is loaded (g.a_rows = slot_src), so no tile waits for anything
@@ -66,19 +65,34 @@ __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
     run_tile_bf16<C, false, R>(g, d, ring, tp);
   });
   // phase 2: the permuted copy x_perm (an output the backward reads), one
-  // row tile per task, filling the workers that the tile tail leaves idle
+  // row tile per task, filling the workers that the tile tail leaves idle.
+  // The task's rows x vectors are one flat range; each thread has kCopyU
+  // 16-byte loads in flight before it stores them.
+  constexpr int kCopyU = 8;
   for (;;) {
     const int task = claim_task(&w.cursor[0], &task_slot);
     if (task >= n_mt) break;
     const int4 mt = w.mtiles[task];
     if (mt.x < g.E) {
-      const uint16_t* x = static_cast<const uint16_t*>(g.x);
-      uint16_t* xp = static_cast<uint16_t*>(g.o_x_perm);
-      for (int r = wave; r < mt.z; r += C::NW) {
-        const int64_t s = mt.y + r;
-        const char* src = reinterpret_cast<const char*>(x + (int64_t)slot_src[s] * g.H);
-        char* dst = reinterpret_cast<char*>(xp + s * g.H);
-        for (int v = lane; v < nvec; v += kWave) st16(dst + (int64_t)v * 16, ld16(src + (int64_t)v * 16));
+      const char* x = static_cast<const char*>(g.x);
+      char* xp = static_cast<char*>(g.o_x_perm);
+      const int total = mt.z * nvec;
+      for (int base = threadIdx.x; base < total; base += C::NT * kCopyU) {
+        u32x4 v[kCopyU];
+#pragma unroll
+        for (int u = 0; u < kCopyU; ++u) {
+          const int idx = min(base + u * C::NT, total - 1);   // past the end: reload the last vector
+          const int row = idx / nvec, c = idx - row * nvec;
+          v[u] = ld16(x + ((int64_t)slot_src[mt.y + row] * nvec + c) * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyU; ++u) {
+          const int idx = base + u * C::NT;
+          if (idx < total) {
+            const int row = idx / nvec, c = idx - row * nvec;
+            st16(xp + ((int64_t)(mt.y + row) * nvec + c) * 16, v[u]);
+          }
+        }
       }
     }
   }
