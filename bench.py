@@ -48,7 +48,7 @@ def parse():
                     help="time the plain calls instead of the fused persistent kernels "
                          "(dispatch+up, down+combine, and the one-launch backward)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-tokens", type=int, default=3072)
     ap.add_argument("--fwd-only", action="store_true")
     ap.add_argument("--no-hbm-flush", action="store_true",
                     help="skip the extra step that times the HBM-bound calls with the caches flushed")
