@@ -6,8 +6,10 @@
 
 namespace moe {
 
-// Tokens per routing chunk: one histogram row and one slot-ranking wave each.
-constexpr int kChunkTokens = 256;
+// Tokens per routing chunk: one histogram row and one slot-ranking wave each
+// (short chunks: the ranking is a chain of dependent ballots per 64 pairs,
+// so more, shorter chains keep more of the GPU busy).
+constexpr int kChunkTokens = 64;
 
 inline int route_nchunk(int T) { return (T + kChunkTokens - 1) / kChunkTokens; }
 

@@ -83,30 +83,33 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 }
 
 // One block per expert: exclusive scan of the expert's column of chunk counts
-// (chunk_base[c][e] = pairs of lower chunks routed to e) and its total.
+// (chunk_base[c][e] = pairs of lower chunks routed to e) and its total.  Each
+// thread sums a contiguous run of chunks, one block scan places the runs.
 __global__ __launch_bounds__(256) void route_chunk_scan_kernel(const int32_t* __restrict__ chunk_counts,
                                                                int nchunk, int E,
                                                                int32_t* __restrict__ chunk_base,
                                                                int32_t* __restrict__ counts) {
   __shared__ int buf[256];
   const int e = blockIdx.x, tid = threadIdx.x;
-  int carry = 0;
-  for (int base = 0; base < nchunk; base += 256) {
-    const int c = base + tid;
-    const int v = c < nchunk ? chunk_counts[(int64_t)c * E + e] : 0;
-    buf[tid] = v;
+  const int per = (nchunk + 255) / 256;
+  const int c0 = min(nchunk, tid * per), c1 = min(nchunk, c0 + per);
+  int mine = 0;
+  for (int c = c0; c < c1; ++c) mine += chunk_counts[(int64_t)c * E + e];
+  buf[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = tid >= off ? buf[tid - off] : 0;
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const int add = tid >= off ? buf[tid - off] : 0;
-      __syncthreads();
-      buf[tid] += add;
-      __syncthreads();
-    }
-    if (c < nchunk) chunk_base[(int64_t)c * E + e] = carry + buf[tid] - v;
-    carry += buf[255];
+    buf[tid] += add;
     __syncthreads();
   }
-  if (tid == 0) counts[e] = carry;
+  int run = buf[tid] - mine;
+  for (int c = c0; c < c1; ++c) {
+    const int v = chunk_counts[(int64_t)c * E + e];
+    chunk_base[(int64_t)c * E + e] = run;
+    run += v;
+  }
+  if (tid == 255) counts[e] = buf[255];
 }
 
 // One wave per chunk.  Expert start offsets = exclusive scan of counts (every
@@ -159,9 +162,11 @@ __global__ __launch_bounds__(64) void route_slot_kernel(const int32_t* __restric
   const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
   const uint64_t lower = (1ull << lane) - 1ull;
   const uint64_t higher = ~((2ull << lane) - 1ull);
+  int e_next = lane < n ? topk_idx[(int64_t)t0 * K + lane] : 0;   // one group of 64 pairs ahead
   for (int q0 = 0; q0 < n; q0 += kWave) {
     const int q = q0 + lane;
-    const int e_in = q < n ? topk_idx[(int64_t)t0 * K + q] : 0;
+    const int e_in = e_next;
+    if (q + kWave < n) e_next = topk_idx[(int64_t)t0 * K + q + kWave];
     const bool act = q < n && (unsigned)e_in < (unsigned)E;   // ids outside [0, E) are skipped
     const int e = act ? e_in : 0;
     uint64_t peers = __ballot(act);
