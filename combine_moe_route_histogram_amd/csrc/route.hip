@@ -5,7 +5,7 @@
 // "deterministic token mapping" / Algorithm 1: a stable sort by expert, the
 // per-expert counts and prefix-sum base offsets give each pair a unique slot
 // without atomic locks.  On one GPU the "ranks" of Algorithm 1 become chunks
-// of 256 tokens: the base of chunk c in expert e is the sum of the counts of
+// of 64 tokens: the base of chunk c in expert e is the sum of the counts of
 // lower chunks for e (exactly the rank-major prefix of the article), and the
 // position inside a chunk is the pair's rank among the chunk's pairs routed to
 // e, taken with wave ballots in (token, k) order.  No atomic decides a slot.
