@@ -25,14 +25,17 @@ __global__ __launch_bounds__(64) void plan_mtiles_kernel(const int32_t* __restri
                                                          int32_t* __restrict__ first_tile,
                                                          int32_t* __restrict__ bands,
                                                          int32_t* __restrict__ clear, int n_clear) {
+  __shared__ int off_s[kMaxExperts + 1];
   const int lane = threadIdx.x;
   const int G = E + Ns;
   const int per = (G + kWave - 1) / kWave;
   const int g_begin = min(G, lane * per), g_end = min(G, g_begin + per);
+  for (int e = lane; e <= E; e += kWave) off_s[e] = offsets[e];   // all loads in flight at once
+  __syncthreads();
   auto group_rows = [&](int grp, int& row0, int& rows) {
     if (grp < E) {
-      row0 = offsets[grp];
-      rows = offsets[grp + 1] - row0;
+      row0 = off_s[grp];
+      rows = off_s[grp + 1] - row0;
     } else {
       row0 = R + (grp - E) * T;
       rows = T;

@@ -11,6 +11,10 @@ namespace moe {
 // so more, shorter chains keep more of the GPU busy).
 constexpr int kChunkTokens = 64;
 
+// Largest number of routed experts (the routing kernels keep one LDS word per
+// expert; the planner stages E + 1 offsets in LDS).
+constexpr int kMaxExperts = 256;
+
 inline int route_nchunk(int T) { return (T + kChunkTokens - 1) / kChunkTokens; }
 
 hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* topk_idx, float* topk_w,

@@ -71,7 +71,8 @@ T* ws_at(void* ws, size_t off) {
 int check_dims(const moe_dims* d) {
   if (!d) return fail(MOE_EINVAL, "dims is NULL");
   if (d->T < 1) return fail(MOE_EINVAL, "T must be >= 1 (got %d)", d->T);
-  if (d->E < 1 || d->E > 256) return fail(MOE_EUNSUPPORTED, "E must be in [1, 256] (got %d)", d->E);
+  if (d->E < 1 || d->E > kMaxExperts)
+    return fail(MOE_EUNSUPPORTED, "E must be in [1, %d] (got %d)", kMaxExperts, d->E);
   if (d->K < 1 || d->K > d->E || d->K > 64)
     return fail(MOE_EUNSUPPORTED, "K must be in [1, min(E, 64)] (got K=%d, E=%d)", d->K, d->E);
   if (d->H <= 0 || d->H % 8)
