@@ -157,7 +157,7 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
     }
     __syncthreads();
     for (int t = t0 + wave; t < t1; t += C::NW)
-      combine_row<uint16_t>(static_cast<const uint16_t*>(g.o_y), slot, topk_w,
+      combine_row<uint16_t, 4, 4, false>(static_cast<const uint16_t*>(g.o_y), slot, topk_w,
                             static_cast<uint16_t*>(g.o_out), t, g.T, g.H, g.K, g.Ns, lane);
   }
 }

@@ -16,31 +16,31 @@ namespace moe {
 constexpr int kRowBlock = 256;               // 4 waves -> 4 tokens per block
 constexpr int kRowsPerBlock = kRowBlock / kWave;
 
-// x_perm[slot[t,k]] = x[t]: each x row is read once and written K times.
+// x_perm[slot[t,k]] = x[t]: each x row is read once (non-temporal: nothing
+// reads it again in this launch) and written K times; 4 vectors per lane per
+// round.
 template <typename S>
 __global__ __launch_bounds__(kRowBlock) void dispatch_kernel(const S* __restrict__ x,
                                                              const int32_t* __restrict__ slot,
                                                              S* __restrict__ x_perm, int T, int H,
                                                              int K) {
+  constexpr int U = 4;
   const int t = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   if (t >= T) return;
   const int my_slot = lane < K ? slot[(int64_t)t * K + lane] : 0;
   const int nvec = H / Elem<S>::kPerVec;
   const char* src = reinterpret_cast<const char*>(x + (int64_t)t * H);
-  for (int v0 = 0; v0 < nvec; v0 += 4 * kWave) {
-    u32x4 val[4];
+  for (int v0 = lane; v0 < nvec; v0 += U * kWave) {
+    u32x4 val[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int v = v0 + u * kWave + lane;
-      if (v < nvec) val[u] = ld16(src + (int64_t)v * 16);
-    }
+    for (int u = 0; u < U; ++u)   // a lane past the row's end reloads its last vector
+      val[u] = ld16_hint<true>(src + (int64_t)min(v0 + u * kWave, nvec - 1) * 16);
     for (int k = 0; k < K; ++k) {
-      const int s = __shfl(my_slot, k, kWave);
-      char* dst = reinterpret_cast<char*>(x_perm + (int64_t)s * H);
+      char* dst = reinterpret_cast<char*>(x_perm + (int64_t)lane_int(my_slot, k) * H);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int v = v0 + u * kWave + lane;
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * kWave;
         if (v < nvec) st16(dst + (int64_t)v * 16, val[u]);
       }
     }
@@ -69,13 +69,15 @@ __global__ __launch_bounds__(kRowBlock) void combine_kernel(const S* __restrict_
                                                             int K, int Ns) {
   const int t = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
   if (t >= T) return;
-  combine_row<S>(y, slot, w, out, t, T, H, K, Ns, threadIdx.x & (kWave - 1));
+  combine_row<S, 4, 4, true>(y, slot, w, out, t, T, H, K, Ns, threadIdx.x & (kWave - 1));
 }
 
 // dy[slot[t,k]] = w[t,k] dout[t];  dw[t,k] = <dout[t], y[slot[t,k]]>.
 // The dot product: per-lane partial sums in vector order, then a fixed
-// butterfly across the wave.  Each lane takes U vectors per round, so 2U
-// loads are in flight (the order of the partial sums is unchanged).
+// butterfly across the wave.  The k rows go in batches of RB: per round a
+// lane loads U vectors of dout and U of each of the batch's y rows together
+// ((RB+1)*U loads in flight), non-temporal; the order of each partial sum is
+// unchanged, so the bits do not depend on U or RB.
 template <typename S>
 __global__ __launch_bounds__(kRowBlock) void combine_bwd_kernel(const S* __restrict__ dout,
                                                                 const S* __restrict__ y,
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(kRowBlock) void combine_bwd_kernel(const S* __restr
                                                                 float* __restrict__ dw, int T,
                                                                 int H, int K) {
   constexpr int P = Elem<S>::kPerVec;
-  constexpr int U = 8;
+  constexpr int U = 4, RB = 4;
   const int t = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   if (t >= T) return;
@@ -93,38 +95,54 @@ __global__ __launch_bounds__(kRowBlock) void combine_bwd_kernel(const S* __restr
   const float my_w = lane < K ? w[(int64_t)t * K + lane] : 0.f;
   const int nvec = H / P;
   const char* g_row = reinterpret_cast<const char*>(dout + (int64_t)t * H);
-  for (int k = 0; k < K; ++k) {
-    const int s = lane_int(my_slot, k);
-    const float wk = lane_float(my_w, k);
-    const char* y_row = reinterpret_cast<const char*>(y + (int64_t)s * H);
-    char* dy_row = reinterpret_cast<char*>(dy + (int64_t)s * H);
-    float part = 0.f;
-    for (int v0 = lane; v0 < nvec; v0 += kWave * U) {
-      u32x4 gr[U], yr[U];
+  for (int k0 = 0; k0 < K; k0 += RB) {
+    float part[RB];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {   // a lane past the row's end reloads its last vector
-        const int64_t v = min(v0 + u * kWave, nvec - 1);
-        gr[u] = ld16(g_row + v * 16);
-        yr[u] = ld16(y_row + v * 16);
+    for (int rb = 0; rb < RB; ++rb) part[rb] = 0.f;
+    for (int v0 = lane; v0 < nvec; v0 += kWave * U) {
+      u32x4 gr[U], yr[RB][U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)   // a lane past the row's end reloads its last vector
+        gr[u] = ld16_hint<true>(g_row + (int64_t)min(v0 + u * kWave, nvec - 1) * 16);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (k0 + rb < K) {
+          const char* y_row = reinterpret_cast<const char*>(y + (int64_t)lane_int(my_slot, k0 + rb) * H);
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            yr[rb][u] = ld16_hint<true>(y_row + (int64_t)min(v0 + u * kWave, nvec - 1) * 16);
+        }
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int v = v0 + u * kWave;
-        if (v < nvec) {
-          float g[P], f[P], o[P];
-          Elem<S>::unpack(gr[u], g);
-          Elem<S>::unpack(yr[u], f);
+      for (int rb = 0; rb < RB; ++rb) {
+        if (k0 + rb < K) {
+          const float wk = lane_float(my_w, k0 + rb);
+          char* dy_row = reinterpret_cast<char*>(dy + (int64_t)lane_int(my_slot, k0 + rb) * H);
 #pragma unroll
-          for (int jj = 0; jj < P; ++jj) {
-            part = fmaf(g[jj], f[jj], part);
-            o[jj] = wk * g[jj];
+          for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * kWave;
+            if (v < nvec) {
+              float g[P], f[P], o[P];
+              Elem<S>::unpack(gr[u], g);
+              Elem<S>::unpack(yr[rb][u], f);
+#pragma unroll
+              for (int jj = 0; jj < P; ++jj) {
+                part[rb] = fmaf(g[jj], f[jj], part[rb]);
+                o[jj] = wk * g[jj];
+              }
+              st16_hint<true>(dy_row + (int64_t)v * 16, Elem<S>::pack(o));
+            }
           }
-          st16(dy_row + (int64_t)v * 16, Elem<S>::pack(o));
         }
       }
     }
-    part = wave_sum(part);
-    if (lane == 0) dw[(int64_t)t * K + k] = part;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (k0 + rb < K) {
+        const float p = wave_sum(part[rb]);
+        if (lane == 0) dw[(int64_t)t * K + k0 + rb] = p;
+      }
+    }
   }
 }
 
@@ -137,7 +155,7 @@ __global__ __launch_bounds__(kRowBlock) void dispatch_bwd_kernel(const S* __rest
                                                                  int K, int Ns) {
   const int t = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
   if (t >= T) return;
-  combine_row<S>(dx_rows, slot, nullptr, dx, t, T, H, K, Ns, threadIdx.x & (kWave - 1));
+  combine_row<S, 4, 4, true>(dx_rows, slot, nullptr, dx, t, T, H, K, Ns, threadIdx.x & (kWave - 1));
 }
 
 // dl[t, e_k] = w_k (dw_k - sum_j w_j dw_j), zero for unselected experts.
