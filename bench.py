@@ -148,7 +148,7 @@ def main():
     def step():
         timed("route", L.route, b, p)
         if fused:
-            timed("dispatch_ffn", M.moe_dispatch_ffn, d, p["x"], b.slot_src, b.offsets, p["w1"],
+            timed("dispatch_ffn", M.moe_dispatch_ffn, d, p["x"], b.slot_src, b.slot, b.offsets, p["w1"],
                   p["w3"], p.get("ws1"), p.get("ws3"), b.x_perm, b.ab, b.h, b.ws)
             timed("ffn_combine", M.moe_ffn_combine, d, b.h, b.offsets, p["w2"], p.get("ws2"),
                   b.slot, b.topk_w, b.y, b.out, b.ws)

@@ -76,7 +76,7 @@ _SIGS = {
     "moe_expert_ffn": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       ctypes.c_size_t, _P]),
     "moe_combine": (ctypes.c_int, [_D, _P, _P, _P, _P, _P]),
-    "moe_dispatch_ffn": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+    "moe_dispatch_ffn": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                         ctypes.c_size_t, _P]),
     "moe_ffn_combine": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_combine_bwd": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P]),
@@ -247,11 +247,13 @@ def moe_combine(d: Dims, y, slot, topk_w, out, stream=None):
           _ptr(out, "out", dt, d.T * d.H), _stream(stream))
 
 
-def moe_dispatch_ffn(d: Dims, x, slot_src, offsets, w1, w3, ws1, ws3, x_perm, ab, h, ws, stream=None):
+def moe_dispatch_ffn(d: Dims, x, slot_src, slot, offsets, w1, w3, ws1, ws3, x_perm, ab, h, ws,
+                     stream=None):
     dt, H, I, E, Ns = d.torch_dtype, d.H, d.I, d.E, d.n_shared
     wp, wn = _ws(ws)
     _call("moe_dispatch_ffn", ctypes.byref(d), _ptr(x, "x", dt, d.T * H),
-          _ptr(slot_src, "slot_src", torch.int32, d.R), _ptr(offsets, "offsets", torch.int32, E + 1),
+          _ptr(slot_src, "slot_src", torch.int32, d.R), _ptr(slot, "slot", torch.int32, d.T * d.K),
+          _ptr(offsets, "offsets", torch.int32, E + 1),
           _ptr(w1, "w1", dt, E * H * I), _ptr(w3, "w3", dt, E * H * I),
           _ptr(ws1, "ws1", dt, Ns * H * I), _ptr(ws3, "ws3", dt, Ns * H * I),
           _ptr(x_perm, "x_perm", dt, d.R * H), _ptr(ab, "ab", dt, d.RA * 2 * I),

@@ -11,7 +11,7 @@
 // from the token rows through the slot map; the gather costs nothing extra
 // and no tile waits.  The expert-contiguous copy x_perm (the backward reads
 // it) is written by tasks after the tiles, on workers the tile tail leaves
-// idle.
+// idle, token by token (each token row read once, written to its K slots).
 //
 // GroupGEMM+Combine.  Combine tasks come after the GEMM tiles; each completed
 // tile adds one to its row tile's counter, and a token is combined once the
@@ -46,15 +46,16 @@ namespace moe {
 using UpCfg = BfPick<kUp>::C;
 using DownCfg = BfPick<kDown>::C;
 
+constexpr int kCopyTokens = 32;  // tokens per x_perm copy task
+
 template <bool R>
 __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
-                                                                  const int32_t* __restrict__ slot_src,
+                                                                  const int32_t* __restrict__ slot,
                                                                   FusedWs w, int nt_count) {
   using C = UpCfg;
   MOE_LDS_RING(C, ring);
   __shared__ int task_slot;
   const int n_mt = *w.n_mtiles;
-  const int nvec = g.H / 8;
   // phase 1: GEMM tiles; the routed rows' A operand is gathered from the token
   // rows as it is loaded (g.a_rows = slot_src), so no tile waits for anything
   for_tasks_xcd_ranges(w.cursor + 1, n_mt * nt_count, 0, 1,
@@ -64,37 +65,20 @@ __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kUp, C::BM, C::BN>(g, tm, tn);
     run_tile_bf16<C, false, R>(g, d, ring, tp);
   });
-  // phase 2: the permuted copy x_perm (an output the backward reads), one
-  // row tile per task, filling the workers that the tile tail leaves idle.
-  // The task's rows x vectors are one flat range; each thread has kCopyU
-  // 16-byte loads in flight before it stores them.
-  constexpr int kCopyU = 8;
+  // phase 2: the permuted copy x_perm (an output the backward reads), token
+  // by token as the plain dispatch does it: each token row is read once and
+  // written to its K slots (a copy by destination row would read every token
+  // row K times).  Tasks of kCopyTokens tokens, one wave per token, fill the
+  // workers that the tile tail leaves idle.
+  const int n_copy = (g.T + kCopyTokens - 1) / kCopyTokens;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   for (;;) {
     const int task = claim_task(&w.cursor[0], &task_slot);
-    if (task >= n_mt) break;
-    const int4 mt = w.mtiles[task];
-    if (mt.x < g.E) {
-      const char* x = static_cast<const char*>(g.x);
-      char* xp = static_cast<char*>(g.o_x_perm);
-      const int total = mt.z * nvec;
-      for (int base = threadIdx.x; base < total; base += C::NT * kCopyU) {
-        u32x4 v[kCopyU];
-#pragma unroll
-        for (int u = 0; u < kCopyU; ++u) {
-          const int idx = min(base + u * C::NT, total - 1);   // past the end: reload the last vector
-          const int row = idx / nvec, c = idx - row * nvec;
-          v[u] = ld16(x + ((int64_t)slot_src[mt.y + row] * nvec + c) * 16);
-        }
-#pragma unroll
-        for (int u = 0; u < kCopyU; ++u) {
-          const int idx = base + u * C::NT;
-          if (idx < total) {
-            const int row = idx / nvec, c = idx - row * nvec;
-            st16(xp + ((int64_t)(mt.y + row) * nvec + c) * 16, v[u]);
-          }
-        }
-      }
-    }
+    if (task >= n_copy) break;
+    const int t1 = min(g.T, (task + 1) * kCopyTokens);
+    for (int t = task * kCopyTokens + wave; t < t1; t += C::NW)
+      dispatch_row<uint16_t, 4, false>(static_cast<const uint16_t*>(g.x), slot,
+                                       static_cast<uint16_t*>(g.o_x_perm), t, g.H, g.K, lane);
   }
 }
 
@@ -162,8 +146,8 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
   }
 }
 
-hipError_t launch_dispatch_ffn(const GemmArgs& a0, const int32_t* slot_src, const FusedWs& w,
-                               hipStream_t st) {
+hipError_t launch_dispatch_ffn(const GemmArgs& a0, const int32_t* slot_src, const int32_t* slot,
+                               const FusedWs& w, hipStream_t st) {
   GemmArgs a = a0;
   a.mtiles = w.mtiles;
   a.n_mtiles = w.n_mtiles;
@@ -175,9 +159,9 @@ hipError_t launch_dispatch_ffn(const GemmArgs& a0, const int32_t* slot_src, cons
   if (e != hipSuccess) return e;
   const int nt = gemm_ntiles<kUp>(a.H, a.I, UpCfg::BN);
   if (ragged_k(a.H, a.I, UpCfg::BK))
-    dispatch_ffn_kernel<true><<<w.workers, UpCfg::NT, 0, st>>>(a, slot_src, w, nt);
+    dispatch_ffn_kernel<true><<<w.workers, UpCfg::NT, 0, st>>>(a, slot, w, nt);
   else
-    dispatch_ffn_kernel<false><<<w.workers, UpCfg::NT, 0, st>>>(a, slot_src, w, nt);
+    dispatch_ffn_kernel<false><<<w.workers, UpCfg::NT, 0, st>>>(a, slot, w, nt);
   return hipGetLastError();
 }
 

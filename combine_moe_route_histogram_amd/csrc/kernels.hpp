@@ -150,7 +150,7 @@ hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int 
                        hipStream_t st);
 
 // Fused persistent kernels (bf16).  ws_* are workspace sections.
-// Task cursors of a fused launch: [0] the gather (dispatch_ffn) or combine
+// Task cursors of a fused launch: [0] the x_perm copy (dispatch_ffn) or combine
 // (ffn_combine) tasks, or the finished first-phase tiles (ffn_bwd); then
 // kXcds tile cursors per GEMM phase (one phase in the forward kernels, four
 // in ffn_bwd).
@@ -167,8 +167,8 @@ struct FusedWs {
   int mt_bound;
   int workers;          // persistent workgroups to launch
 };
-hipError_t launch_dispatch_ffn(const GemmArgs& a, const int32_t* slot_src, const FusedWs& w,
-                               hipStream_t st);
+hipError_t launch_dispatch_ffn(const GemmArgs& a, const int32_t* slot_src, const int32_t* slot,
+                               const FusedWs& w, hipStream_t st);
 hipError_t launch_ffn_combine(const GemmArgs& a, const int32_t* slot, const float* topk_w,
                               const FusedWs& w, hipStream_t st);
 // Expert-FFN backward in one persistent launch (bwd.hip): activation-gradient

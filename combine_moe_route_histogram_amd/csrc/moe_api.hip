@@ -354,12 +354,13 @@ int moe_combine(const moe_dims* d, const void* y, const int32_t* slot, const flo
 }
 
 int moe_dispatch_ffn(const moe_dims* d, const void* x, const int32_t* slot_src,
-                     const int32_t* offsets, const void* w1, const void* w3, const void* ws1,
-                     const void* ws3, void* x_perm, void* ab, void* h, void* ws, size_t ws_bytes,
-                     void* stream) {
+                     const int32_t* slot, const int32_t* offsets, const void* w1, const void* w3,
+                     const void* ws1, const void* ws3, void* x_perm, void* ab, void* h, void* ws,
+                     size_t ws_bytes, void* stream) {
   MOE_TRY(check_dims(d));
   MOE_TRY(check_ptr(x, "x"));
   MOE_TRY(check_ptr(slot_src, "slot_src"));
+  MOE_TRY(check_ptr(slot, "slot"));
   MOE_TRY(check_ptr(offsets, "offsets"));
   MOE_TRY(check_ptr(w1, "w1"));
   MOE_TRY(check_ptr(w3, "w3"));
@@ -385,7 +386,7 @@ int moe_dispatch_ffn(const moe_dims* d, const void* x, const int32_t* slot_src,
   a.o_ab = ab; a.o_h = h;
   FusedWs w;
   MOE_TRY(fused_ws(d, ws, &w));
-  return hip_status(launch_dispatch_ffn(a, slot_src, w, st), "moe_dispatch_ffn");
+  return hip_status(launch_dispatch_ffn(a, slot_src, slot, w, st), "moe_dispatch_ffn");
 }
 
 int moe_ffn_combine(const moe_dims* d, const void* h, const int32_t* offsets, const void* w2,

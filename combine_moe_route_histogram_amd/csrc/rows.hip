@@ -17,34 +17,15 @@ constexpr int kRowBlock = 256;               // 4 waves -> 4 tokens per block
 constexpr int kRowsPerBlock = kRowBlock / kWave;
 
 // x_perm[slot[t,k]] = x[t]: each x row is read once (non-temporal: nothing
-// reads it again in this launch) and written K times; 4 vectors per lane per
-// round.
+// reads it again in this launch) and written K times.
 template <typename S>
 __global__ __launch_bounds__(kRowBlock) void dispatch_kernel(const S* __restrict__ x,
                                                              const int32_t* __restrict__ slot,
                                                              S* __restrict__ x_perm, int T, int H,
                                                              int K) {
-  constexpr int U = 4;
   const int t = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
   if (t >= T) return;
-  const int my_slot = lane < K ? slot[(int64_t)t * K + lane] : 0;
-  const int nvec = H / Elem<S>::kPerVec;
-  const char* src = reinterpret_cast<const char*>(x + (int64_t)t * H);
-  for (int v0 = lane; v0 < nvec; v0 += U * kWave) {
-    u32x4 val[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u)   // a lane past the row's end reloads its last vector
-      val[u] = ld16_hint<true>(src + (int64_t)min(v0 + u * kWave, nvec - 1) * 16);
-    for (int k = 0; k < K; ++k) {
-      char* dst = reinterpret_cast<char*>(x_perm + (int64_t)lane_int(my_slot, k) * H);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int v = v0 + u * kWave;
-        if (v < nvec) st16(dst + (int64_t)v * 16, val[u]);
-      }
-    }
-  }
+  dispatch_row<S, 4, true>(x, slot, x_perm, t, H, K, threadIdx.x & (kWave - 1));
 }
 
 // x_perm[s] = x[slot_src[s]]: the same rows as dispatch, indexed by destination.

@@ -87,4 +87,29 @@ __device__ __forceinline__ void combine_row(const S* __restrict__ y, const int32
   }
 }
 
+// x_perm[slot[t,k]] = x[t] for k = 0..K-1: the token row is read once (U
+// 16-byte vectors per lane per round) and written to its K slots.  NT:
+// non-temporal loads (the plain launch, where nothing reads the row again).
+template <typename S, int U, bool NT>
+__device__ __forceinline__ void dispatch_row(const S* __restrict__ x, const int32_t* __restrict__ slot,
+                                             S* __restrict__ x_perm, int t, int H, int K, int lane) {
+  const int my_slot = lane < K ? slot[(int64_t)t * K + lane] : 0;
+  const int nvec = H / Elem<S>::kPerVec;
+  const char* src = reinterpret_cast<const char*>(x + (int64_t)t * H);
+  for (int v0 = lane; v0 < nvec; v0 += U * kWave) {
+    u32x4 val[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)   // a lane past the row's end reloads its last vector
+      val[u] = ld16_hint<NT>(src + (int64_t)min(v0 + u * kWave, nvec - 1) * 16);
+    for (int k = 0; k < K; ++k) {
+      char* dst = reinterpret_cast<char*>(x_perm + (int64_t)lane_int(my_slot, k) * H);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * kWave;
+        if (v < nvec) st16(dst + (int64_t)v * 16, val[u]);
+      }
+    }
+  }
+}
+
 }  // namespace moe

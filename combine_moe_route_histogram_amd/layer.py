@@ -65,7 +65,7 @@ def forward(b: Buffers, p: dict, fused: bool = False, stream=None):
     d = b.d
     route(b, p, stream)
     if fused:
-        moe_dispatch_ffn(d, p["x"], b.slot_src, b.offsets, p["w1"], p["w3"], p.get("ws1"),
+        moe_dispatch_ffn(d, p["x"], b.slot_src, b.slot, b.offsets, p["w1"], p["w3"], p.get("ws1"),
                          p.get("ws3"), b.x_perm, b.ab, b.h, b.ws, stream)
         moe_ffn_combine(d, b.h, b.offsets, p["w2"], p.get("ws2"), b.slot, b.topk_w, b.y, b.out,
                         b.ws, stream)

@@ -179,16 +179,21 @@ int moe_combine(const moe_dims* d, const void* y, const int32_t* slot, const flo
                 void* out, void* stream);
 
 /* Fused Dispatch+GroupGEMM (UniEP section 2.1/2.2 MegaKernel): one persistent
- * launch whose workers claim tasks from one atomic cursor -- first the gather
- * tasks (copy the rows of one 128/256-row tile of x_perm from x via slot_src
- * and publish a per-tile ready flag), then the GEMM tiles of
- * moe_expert_ffn_up, each waiting only on the flag of its own row tile.
+ * launch whose workers claim tasks from atomic cursors.  The GEMM tiles of
+ * moe_expert_ffn_up come first; each reads its routed rows straight from the
+ * token rows x through slot_src as it loads its A operand, so no tile waits
+ * for a gather.  Then copy tasks write the expert-contiguous rows x_perm
+ * (which the backward reads) token by token: each token row of x is read once
+ * and written to its K rows slot[t, 0..K-1].  slot_src [R] and slot [T, K]
+ * are moe_route's outputs for the same routing.
  * Outputs (x_perm, ab, h) are bit-identical to moe_dispatch followed by
- * moe_expert_ffn_up. */
+ * moe_expert_ffn_up.  f32, or bf16 with T*H*2 bytes above 2^31 - 64 KiB (the
+ * kernel's per-lane byte offsets into x are 32-bit): a plain gather, then
+ * moe_expert_ffn_up, with the same results. */
 int moe_dispatch_ffn(const moe_dims* d, const void* x, const int32_t* slot_src,
-                     const int32_t* offsets, const void* w1, const void* w3, const void* ws1,
-                     const void* ws3, void* x_perm, void* ab, void* h, void* ws, size_t ws_bytes,
-                     void* stream);
+                     const int32_t* slot, const int32_t* offsets, const void* w1, const void* w3,
+                     const void* ws1, const void* ws3, void* x_perm, void* ab, void* h, void* ws,
+                     size_t ws_bytes, void* stream);
 
 /* Fused GroupGEMM+Combine (UniEP section 2.1 second MegaKernel): the GEMM
  * tiles of moe_expert_ffn_down, then combine tasks that wait on per-row-tile
