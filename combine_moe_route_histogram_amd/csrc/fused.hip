@@ -118,28 +118,48 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
     band_order_groups(tp.L, nt_count, w.bands, w.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kDown, C::BM, C::BN>(g, tm, tn);
     run_tile_bf16<C, true, R>(g, d, ring, tp);
-    if (tp.part == tp.parts - 1) publish_add(&w.flags[tm]);   // the tile is complete
+    if (tp.part == tp.parts - 1)   // the tile is complete
+      publish_add(&w.flags[tm], &w.cursor[kTilesDone]);
   });
-  // phase 2: combine tasks, each token once all its rows' tiles are done
+  // phase 2: combine tasks, each token once all its rows' tiles are done.
+  // A worker that finds every tile published takes one acquire and then runs
+  // all its remaining tasks without polls or further acquires (an agent-scope
+  // acquire invalidates the XCD's whole L2, so one per task would cost the
+  // tiles still running there their operands).
+  __shared__ int all_done_s;
+  bool all_done = false;   // uniform over the workgroup
+  const int n_tiles = n_mt * nt_count;
   for (;;) {
     const int task = claim_task(&w.cursor[0], &task_slot);
     if (task >= n_comb) break;
     const int t0 = task * kCombineTokens;
     const int t1 = min(g.T, t0 + kCombineTokens);
-    // wave 0 waits until the row tiles holding the task's routed rows (q < K)
-    // and shared-expert rows (q >= K) are all complete, then one acquire
-    if (wave == 0) {
-      const int nq = g.K + g.Ns;
-      for (int i = lane; i < (t1 - t0) * nq; i += kWave) {
-        const int t = t0 + i / nq, q = i - (i / nq) * nq;
-        const int64_t row = q < g.K ? (int64_t)slot[(int64_t)t * g.K + q]
-                                    : g.R + (int64_t)(q - g.K) * g.T + t;
-        const int tile = tile_of_row(row, g, w.first_tile, C::BM);
-        poll_at_least(g, &w.flags[tile], nt_count);
+    if (!all_done) {
+      // wave 0: unless every tile is published, wait until the row tiles
+      // holding the task's routed rows (q < K) and shared-expert rows (q >= K)
+      // are complete; then one acquire
+      if (wave == 0) {
+        int done = 0;
+        if (lane == 0)
+          done = __hip_atomic_load(&w.cursor[kTilesDone], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT) >= n_tiles + g.wait_extra;
+        done = __builtin_amdgcn_readfirstlane(done);
+        if (!done) {
+          const int nq = g.K + g.Ns;
+          for (int i = lane; i < (t1 - t0) * nq; i += kWave) {
+            const int t = t0 + i / nq, q = i - (i / nq) * nq;
+            const int64_t row = q < g.K ? (int64_t)slot[(int64_t)t * g.K + q]
+                                        : g.R + (int64_t)(q - g.K) * g.T + t;
+            const int tile = tile_of_row(row, g, w.first_tile, C::BM);
+            poll_at_least(g, &w.flags[tile], nt_count);
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (lane == 0) all_done_s = done;
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __syncthreads();
+      all_done = __builtin_amdgcn_readfirstlane(all_done_s) != 0;
     }
-    __syncthreads();
     for (int t = t0 + wave; t < t1; t += C::NW)
       combine_row<uint16_t, 4, 4, false>(static_cast<const uint16_t*>(g.o_y), slot, topk_w,
                             static_cast<uint16_t*>(g.o_out), t, g.T, g.H, g.K, g.Ns, lane);

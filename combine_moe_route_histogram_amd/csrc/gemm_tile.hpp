@@ -692,18 +692,21 @@ struct TaskPart {
 
 // Publish data written with agent-coherent stores (st_agent_*): every wave
 // waits until its stores have completed (vmcnt 0: each is then coherent at
-// device scope), then thread 0 counts the publish with an agent-scope atomic.
+// device scope), then thread 0 counts the publish with an agent-scope atomic
+// (on a second counter as well, if one is given).
 // No release fence: the data a reader of this counter consumes is coherent
 // already, and a release would write back the XCD's whole L2.  Readers poll
 // the counter and then take one agent-scope acquire (which invalidates their
 // L2's non-coherent lines) before reading.  The trailing barrier keeps thread
 // 0's publish and a following claim in separate convergent regions, so the
 // compiler cannot merge them across a loop edge into a thread-0-only path.
-__device__ __forceinline__ void publish_add(int32_t* counter) {
+__device__ __forceinline__ void publish_add(int32_t* counter, int32_t* counter2 = nullptr) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0)
+  if (threadIdx.x == 0) {
     __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (counter2) __hip_atomic_fetch_add(counter2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   __syncthreads();
 }
 

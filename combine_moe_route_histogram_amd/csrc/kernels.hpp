@@ -153,10 +153,11 @@ hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int 
 // Task cursors of a fused launch: [0] the x_perm copy (dispatch_ffn) or combine
 // (ffn_combine) tasks, or the finished first-phase tiles (ffn_bwd); then
 // kXcds tile cursors per GEMM phase (one phase in the forward kernels, four
-// in ffn_bwd).
+// in ffn_bwd); last, [kTilesDone]: GEMM tiles published so far (ffn_combine).
 constexpr int kXcds = 8;
 constexpr int kMaxPhases = 4;
-constexpr int kFusedCursors = 1 + kMaxPhases * kXcds;
+constexpr int kFusedCursors = 2 + kMaxPhases * kXcds;
+constexpr int kTilesDone = kFusedCursors - 1;
 struct FusedWs {
   int4* mtiles;
   int32_t* n_mtiles;
