@@ -90,7 +90,7 @@ void ffn_bwd_kernel(GemmArgs g, FusedWs w) {
   // phase 2: dW2
   for_tasks_xcd_ranges(cur + kXcds, mt_wd * nt_wd, 0, 1, &task_slot, [&](const TaskPart& tp) {
     int tm, tn;
-    band_order(tp.L, mt_wd, nt_wd, tm, tn);
+    band_order<kWgDown>(tp.L, mt_wd, nt_wd, tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kWgDown, WdCfg::BM, WdCfg::BN>(g, tm, tn);
     if (!d.skip) run_tile_bf16<WdCfg, false, R>(g, d, ring, tp);
   });
@@ -110,7 +110,7 @@ void ffn_bwd_kernel(GemmArgs g, FusedWs w) {
   // phase 4: dW1 | dW3
   for_tasks_xcd_ranges(cur + 3 * kXcds, mt_wu * nt_wu, 0, 1, &task_slot, [&](const TaskPart& tp) {
     int tm, tn;
-    band_order(tp.L, mt_wu, nt_wu, tm, tn);
+    band_order<kWgUp>(tp.L, mt_wu, nt_wu, tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kWgUp, WuCfg::BM, WuCfg::BN>(g, tm, tn);
     if (!d.skip) run_tile_bf16<WuCfg, false, R>(g, d, ring, tp);
   });

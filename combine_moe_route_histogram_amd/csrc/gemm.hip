@@ -109,7 +109,7 @@ void gemm_bf16_kernel(GemmArgs g, int mt_fixed, int nt_count, int32_t* cursors, 
                        [&](const TaskPart& tp) {
     int tm, tn;
     if constexpr (KindTraits<C::KIND>::kWgrad)
-      band_order(tp.L, mt_count, nt_count, tm, tn);
+      band_order<C::KIND>(tp.L, mt_count, nt_count, tm, tn);
     else
       band_order_groups(tp.L, nt_count, g.bands, g.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, C::KIND, C::BM, C::BN>(g, tm, tn);

@@ -1033,17 +1033,26 @@ __device__ void run_tile_f32(const GemmArgs& g, const TileDesc<float>& d, float*
 constexpr int kF32LdsFloats = kF32BK * (kF32BM + 4) + kF32BK * (kF32BN + 4);
 
 // Logical tile -> (row tile, column tile).  Row tiles are taken in bands of
-// kBandM; inside a band the column tiles advance slowest, so the tiles an XCD
-// runs at the same time form a kBandM x (concurrent / kBandM) block: each
-// operand slice they load is shared by several of them through L2.
+// kBandM (the forward and input-gradient kinds, over each group's row tiles)
+// or WgradBand<KIND> (the weight-gradient kinds' fixed grid, whose M tiles
+// are H blocks for dW1/dW3 and I blocks for dW2); inside a band the column
+// tiles advance slowest, so the tiles an XCD runs at the same time form a
+// band x (concurrent / band) block: each operand slice they load is shared
+// by several of them through L2.  The heights were chosen by measurement.
 constexpr int kBandM = 8;
+template <int KIND>
+struct WgradBand {
+  static constexpr int value = KIND == kWgUp ? 4 : 8;
+};
+template <int KIND>
 __device__ __forceinline__ void band_order(int L, int mt_count, int nt_count, int& tm, int& tn) {
-  const int band_tiles = kBandM * nt_count;
+  constexpr int kB = WgradBand<KIND>::value;
+  const int band_tiles = kB * nt_count;
   const int band = L / band_tiles;
   const int rem = L - band * band_tiles;
-  const int rows = min(kBandM, mt_count - band * kBandM);
+  const int rows = min(kB, mt_count - band * kB);
   tn = rem / rows;
-  tm = band * kBandM + (rem - tn * rows);
+  tm = band * kB + (rem - tn * rows);
 }
 
 // ------------------------------------------------------- tile scheduling ----
