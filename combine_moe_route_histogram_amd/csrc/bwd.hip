@@ -123,7 +123,8 @@ hipError_t launch_ffn_bwd(const GemmArgs& a0, const FusedWs& w, hipStream_t st) 
   a.bands = w.bands;
   a.mt_max = w.mt_bound;
   // row tiles, bands, and every counter and cursor of the launch cleared
-  hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, BuCfg::BM, w.mtiles, w.n_mtiles,
+  hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, BuCfg::BM, big_group_band(kBwdUp),
+                             w.mtiles, w.n_mtiles,
                              nullptr, w.bands, w.flags,
                              w.mt_bound + kFusedCursors + kXcds * kSplitWr, st);
   if (e != hipSuccess) return e;

@@ -173,7 +173,8 @@ hipError_t launch_dispatch_ffn(const GemmArgs& a0, const int32_t* slot_src, cons
   a.n_mtiles = w.n_mtiles;
   a.bands = w.bands;
   a.a_rows = slot_src;
-  hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, UpCfg::BM, w.mtiles, w.n_mtiles,
+  hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, UpCfg::BM, big_group_band(kUp),
+                             w.mtiles, w.n_mtiles,
                              w.first_tile, w.bands, w.flags,
                              w.mt_bound + kFusedCursors + kXcds * kSplitWr, st);
   if (e != hipSuccess) return e;
@@ -191,7 +192,8 @@ hipError_t launch_ffn_combine(const GemmArgs& a0, const int32_t* slot, const flo
   a.mtiles = w.mtiles;
   a.n_mtiles = w.n_mtiles;
   a.bands = w.bands;
-  hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, DownCfg::BM, w.mtiles, w.n_mtiles,
+  hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, DownCfg::BM, big_group_band(kDown),
+                             w.mtiles, w.n_mtiles,
                              w.first_tile, w.bands, w.flags,
                              w.mt_bound + kFusedCursors + kXcds * kSplitWr, st);
   if (e != hipSuccess) return e;

@@ -14,12 +14,13 @@ namespace moe {
 
 // Row-tile table: per group (E routed experts, then Ns shared experts over
 // all T tokens) ceil(rows / bm) entries {group, first row, rows, 0}, groups in
-// order; n_mtiles[0] = number of entries.  Band table: each group's row tiles
-// in runs of at most kBandM, bands[b] = first row tile of band b, bands[nb] =
+// order; n_mtiles[0] = number of entries.  Band table: a group of at most
+// kBandM row tiles is one band, a larger one runs of `big` row tiles
+// (group_bands); bands[b] = first row tile of band b, bands[nb] =
 // n_mtiles[0], n_mtiles[1] = nb.  One wave: each lane owns a contiguous run of
 // groups, wave scans give every lane its first table indices.
 __global__ __launch_bounds__(64) void plan_mtiles_kernel(const int32_t* __restrict__ offsets, int E,
-                                                         int Ns, int T, int R, int bm,
+                                                         int Ns, int T, int R, int bm, int big,
                                                          int4* __restrict__ mtiles,
                                                          int32_t* __restrict__ n_mtiles,
                                                          int32_t* __restrict__ first_tile,
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(64) void plan_mtiles_kernel(const int32_t* __restri
     group_rows(grp, row0, rows);
     const int mt = (rows + bm - 1) / bm;
     mine += mt;
-    mine_b += (mt + kBandM - 1) / kBandM;
+    mine_b += group_bands(mt, big);
   }
   int incl = mine, incl_b = mine_b;
 #pragma unroll
@@ -65,7 +66,8 @@ __global__ __launch_bounds__(64) void plan_mtiles_kernel(const int32_t* __restri
     group_rows(grp, row0, rows);
     if (first_tile) first_tile[grp] = idx;
     const int mt = (rows + bm - 1) / bm;
-    for (int c = 0; c < mt; c += kBandM) bands[bidx++] = idx + c;
+    const int step = mt <= kBandM ? kBandM : big;
+    for (int c = 0; c < mt; c += step) bands[bidx++] = idx + c;
     for (int r = 0; r < rows; r += bm) mtiles[idx++] = make_int4(grp, row0 + r, min(bm, rows - r), 0);
   }
   if (lane == kWave - 1) {
@@ -76,10 +78,10 @@ __global__ __launch_bounds__(64) void plan_mtiles_kernel(const int32_t* __restri
   for (int i = lane; i < n_clear; i += kWave) clear[i] = 0;
 }
 
-hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int bm, int4* mtiles,
-                       int32_t* n_mtiles, int32_t* first_tile, int32_t* bands, int32_t* clear,
-                       int n_clear, hipStream_t st) {
-  plan_mtiles_kernel<<<1, 64, 0, st>>>(offsets, E, Ns, T, R, bm, mtiles, n_mtiles, first_tile,
+hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int bm, int big,
+                       int4* mtiles, int32_t* n_mtiles, int32_t* first_tile, int32_t* bands,
+                       int32_t* clear, int n_clear, hipStream_t st) {
+  plan_mtiles_kernel<<<1, 64, 0, st>>>(offsets, E, Ns, T, R, bm, big, mtiles, n_mtiles, first_tile,
                                        bands, clear, n_clear);
   return hipGetLastError();
 }
@@ -141,8 +143,8 @@ static hipError_t launch_kind(bool is_bf16, GemmArgs a, int4* mtiles_ws, int32_t
   int mt_count;
   if constexpr (!KindTraits<KIND>::kWgrad) {
     // the tile cursors and, kFusedCursors - 1 ints on, the split counters
-    plan_mtiles_kernel<<<1, 64, 0, st>>>(a.offsets, a.E, a.Ns, a.T, a.R, BM, mtiles_ws, n_ws,
-                                         nullptr, bands_ws, cursors,
+    plan_mtiles_kernel<<<1, 64, 0, st>>>(a.offsets, a.E, a.Ns, a.T, a.R, BM, big_group_band(KIND),
+                                         mtiles_ws, n_ws, nullptr, bands_ws, cursors,
                                          is_bf16 ? (kFusedCursors - 1) + kXcds * kSplitWr : 0);
     a.mtiles = mtiles_ws;
     a.n_mtiles = n_ws;

@@ -1040,6 +1040,19 @@ constexpr int kF32LdsFloats = kF32BK * (kF32BM + 4) + kF32BK * (kF32BN + 4);
 // band x (concurrent / band) block: each operand slice they load is shared
 // by several of them through L2.  The heights were chosen by measurement.
 constexpr int kBandM = 8;
+// Row-tile bands of the forward and input-gradient kinds: a group of at most
+// kBandM row tiles is one band (its weights are then read by one band only);
+// a larger group is cut into bands of big_group_band(kind) row tiles -- 4,
+// so the band's token rows stay in L2 across its column tiles, except for
+// the down projection, whose short k rows make its weights the larger
+// operand (measured: 4 is 3-5 % faster than 8 for the up projection and
+// both input-side backward GEMMs at 64 row tiles per expert, 3 % slower for
+// the down projection; a 5-row-tile expert split into bands of 4 and 1 reads
+// its weights twice and runs 6 % slower).
+__host__ __device__ constexpr int big_group_band(int kind) { return kind == kDown ? kBandM : 4; }
+__host__ __device__ inline int group_bands(int mt, int big) {
+  return mt <= 0 ? 0 : mt <= kBandM ? 1 : (mt + big - 1) / big;
+}
 template <int KIND>
 struct WgradBand {
   static constexpr int value = KIND == kWgUp ? 4 : 8;

@@ -59,8 +59,8 @@ struct GemmArgs {
   const int32_t* offsets;  // [E+1] routed row ranges
   const int4* mtiles;      // per M-tile {group, first row (all-rows index), rows, 0}
   const int32_t* n_mtiles; // [0] valid entries in mtiles, [1] number of bands
-  const int32_t* bands;    // [bands + 1] first M-tile of each band: a group's M-tiles in runs
-                           // of at most kBandM (the last entry is the M-tile count)
+  const int32_t* bands;    // [bands + 1] first M-tile of each band (group_bands: a group of at most
+                           // kBandM M-tiles is one band; the last entry is the M-tile count)
   int mt_max;              // host bound on the number of M-tiles
   const void* x_perm;
   const void* x;
@@ -144,10 +144,9 @@ hipError_t launch_gemm(bool is_bf16, int kind, const GemmArgs& a, int4* mtiles_w
 // Row-tile planner (one wave): table of bm-row tiles per group, the first
 // table index of every group (if first_tile), and n_clear ints of `clear` set
 // to zero (flags and cursors of the fused kernels).
-hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int bm, int4* mtiles,
-                       int32_t* n_mtiles, int32_t* first_tile, int32_t* bands, int32_t* clear,
-                       int n_clear,
-                       hipStream_t st);
+hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int bm, int big,
+                       int4* mtiles, int32_t* n_mtiles, int32_t* first_tile, int32_t* bands,
+                       int32_t* clear, int n_clear, hipStream_t st);
 
 // Fused persistent kernels (bf16).  ws_* are workspace sections.
 // Task cursors of a fused launch: [0] the x_perm copy (dispatch_ffn) or combine
