@@ -25,6 +25,7 @@ SHAPES = [
     (200, 200, 6, 2, 136, 0),     # H, I not whole k slices
     (64, 64, 4, 4, 64, 0),        # K = E: every expert holds every token
     (40, 128, 256, 8, 64, 0),     # 256 experts, most of them empty
+    (2400, 64, 1, 1, 64, 1),      # groups of 10 row tiles: split into several bands
 ]
 OUTS = ("x_perm", "ab", "h", "y", "out")
 

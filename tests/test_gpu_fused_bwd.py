@@ -25,6 +25,7 @@ SHAPES = [
     (150, 72, 4, 2, 88, 1),       # H, I not whole k slices, a shared expert
     (64, 64, 4, 4, 64, 0),        # K = E
     (40, 128, 256, 8, 64, 1),     # 256 experts, most empty, a shared expert
+    (2400, 64, 1, 1, 64, 1),      # groups of 10 row tiles: split into several bands
 ]
 OUTS = ("dab", "dx_rows", "dw1", "dw3", "dw2", "dws1", "dws3", "dws2", "dx", "dtopk_w", "dlogits")
 

@@ -29,6 +29,8 @@ SHAPES = [
     (96, 64, 32, 20, 64, 1),      # more rows per token than 16-byte vectors per row
     (200, 200, 6, 2, 136, 0),     # H, I multiples of 8, not of the 64-wide k slice
     (150, 72, 4, 2, 88, 1),       # the same with a shared expert
+    (2400, 64, 1, 1, 64, 1),      # groups of 10 row tiles: split into several bands
+    (2200, 64, 2, 2, 64, 0),      # two experts of 2200 rows (9 row tiles) each
 ]
 
 
