@@ -76,7 +76,7 @@ void ffn_bwd_kernel(GemmArgs g, FusedWs w) {
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kBwdUp, BuCfg::BM, BuCfg::BN>(g, tm, tn);
     if (!d.skip) run_tile_bf16<BuCfg, false, R>(g, d, ring, tp);
     ++mine;
-  });
+  }, g.perturb);
   // publish this worker's phase-1 rows: own stores complete, one release,
   // then the count
   __builtin_amdgcn_s_waitcnt(0);
@@ -93,7 +93,7 @@ void ffn_bwd_kernel(GemmArgs g, FusedWs w) {
     band_order<kWgDown>(tp.L, mt_wd, nt_wd, tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kWgDown, WdCfg::BM, WdCfg::BN>(g, tm, tn);
     if (!d.skip) run_tile_bf16<WdCfg, false, R>(g, d, ring, tp);
-  });
+  }, g.perturb);
 
   // phases 3 and 4 read phase 1's output
   wait_count(g, p1_done, n_mt * nt_bu);
@@ -105,7 +105,7 @@ void ffn_bwd_kernel(GemmArgs g, FusedWs w) {
     band_order_groups(tp.L, nt_bd, g.bands, g.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kBwdDown, BdCfg::BM, BdCfg::BN>(g, tm, tn);
     if (!d.skip) run_tile_bf16<BdCfg, false, R>(g, d, ring, tp);
-  });
+  }, g.perturb);
 
   // phase 4: dW1 | dW3
   for_tasks_xcd_ranges(cur + 3 * kXcds, mt_wu * nt_wu, 0, 1, &task_slot, [&](const TaskPart& tp) {
@@ -113,7 +113,7 @@ void ffn_bwd_kernel(GemmArgs g, FusedWs w) {
     band_order<kWgUp>(tp.L, mt_wu, nt_wu, tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kWgUp, WuCfg::BM, WuCfg::BN>(g, tm, tn);
     if (!d.skip) run_tile_bf16<WuCfg, false, R>(g, d, ring, tp);
-  });
+  }, g.perturb);
 }
 
 hipError_t launch_ffn_bwd(const GemmArgs& a0, const FusedWs& w, hipStream_t st) {

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
     band_order_groups(tp.L, nt_count, w.bands, w.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kUp, C::BM, C::BN>(g, tm, tn);
     run_tile_bf16<C, false, R>(g, d, ring, tp);
-  });
+  }, g.perturb);
   // phase 2: the permuted copy x_perm (an output the backward reads), token
   // by token as the plain dispatch does it: each token row is read once and
   // written to its K slots (a copy by destination row would read every token
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
     run_tile_bf16<C, true, R>(g, d, ring, tp);
     if (tp.part == tp.parts - 1)   // the tile is complete
       publish_add(&w.flags[tm], &w.cursor[kTilesDone]);
-  });
+  }, g.perturb);
   // phase 2: combine tasks, each token once all its rows' tiles are done.
   // A worker that finds every tile published takes one acquire and then runs
   // all its remaining tasks without polls or further acquires (an agent-scope

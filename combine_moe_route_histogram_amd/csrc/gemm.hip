@@ -116,7 +116,7 @@ void gemm_bf16_kernel(GemmArgs g, int mt_fixed, int nt_count, int32_t* cursors, 
       band_order_groups(tp.L, nt_count, g.bands, g.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, C::KIND, C::BM, C::BN>(g, tm, tn);
     if (!d.skip) run_tile_bf16<C, false, R>(g, d, ring, tp);
-  });
+  }, g.perturb);
 }
 
 __global__ __launch_bounds__(64) void clear_i32_kernel(int32_t* p, int n) {

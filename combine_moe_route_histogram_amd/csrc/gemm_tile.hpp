@@ -1119,24 +1119,57 @@ __device__ __forceinline__ RangePlan range_plan(int r, int n, int wr, int max_pa
   return p;
 }
 
+// Debug perturbation of the schedule (GemmArgs::perturb, determinism tests).
+__device__ __forceinline__ uint32_t perturb_hash(uint32_t x) {
+  x ^= x >> 16; x *= 0x7FEB352Du; x ^= x >> 15; x *= 0x846CA68Bu; x ^= x >> 16;
+  return x;
+}
+// Sleep 0..7 x 32 x 64 clocks, chosen by (seed, worker, claim count).
+__device__ __forceinline__ void perturb_delay(uint32_t seed, uint32_t claims) {
+  const uint32_t h = perturb_hash(seed ^ perturb_hash(blockIdx.x * 0x9E3779B1u + claims));
+  for (uint32_t i = 0; i < (h & 7u); ++i) __builtin_amdgcn_s_sleep(32);
+}
+// Affine bijection t -> (a t + c) mod n of [0, n): a seeded multiplier made
+// coprime to n.
+__device__ __forceinline__ void perturb_affine(uint32_t seed, int r, int n, int& a, int& c) {
+  a = 1; c = 0;
+  if (n <= 1) return;
+  const uint32_t h = perturb_hash(seed * 0x85EBCA77u + (uint32_t)r);
+  c = (int)(h % (uint32_t)n);
+  a = (int)(perturb_hash(h) % (uint32_t)n) | 1;
+  for (;;) {   // smallest a' >= a with gcd(a', n) = 1 (a' = n + 1 at the latest)
+    int x = a, y = n;
+    while (y) { const int z = x % y; x = y; y = z; }
+    if (x == 1) break;
+    ++a;
+  }
+}
+
 // Run every task of the ranges, own XCD's range first.  wr = 0: whole tiles
 // only; otherwise tail tiles are split as above (max_parts: slices per tile).
+// perturb (debug, nonzero): each range's whole tiles are claimed in a seeded
+// order and every claim is preceded by a seeded sleep; split tails keep their
+// order (helpers before owners), so every wait still ends.
 template <class F>
 __device__ __forceinline__ void for_tasks_xcd_ranges(int32_t* cursors, int n, int wr, int max_parts,
-                                                     int* slot, F&& task) {
+                                                     int* slot, F&& task, uint32_t perturb = 0) {
   const int home = blockIdx.x % kXcds;
+  uint32_t claims = 0;
   for (int q = 0; q < kXcds; ++q) {
     const int r = (home + q) % kXcds;
     const RangePlan p = range_plan(r, n, wr, max_parts);
     const int whole = p.split_from - p.lo;
     const int total = whole + (p.hi - p.split_from) * p.parts;
+    int pa = 1, pc = 0;
+    if (perturb) perturb_affine(perturb, r, whole, pa, pc);
     for (;;) {
+      if (perturb) perturb_delay(perturb, claims++);
       const int t = claim_task(&cursors[r], slot);
       if (t >= total) break;
       TaskPart tp;
       tp.range = r;
       if (t < whole) {
-        tp.L = p.lo + t;
+        tp.L = p.lo + (perturb ? (int)(((int64_t)t * pa + pc) % whole) : t);
         tp.part = 0;
         tp.parts = 1;
         tp.slot = 0;

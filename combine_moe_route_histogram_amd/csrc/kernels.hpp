@@ -98,6 +98,10 @@ struct GemmArgs {
   // wait_extra (debug, 0 or 1) is added to every wait's target
   uint64_t wait_ticks;
   int wait_extra;
+  // debug (determinism tests): nonzero = persistent workers claim each
+  // range's whole tiles in a seeded order and sleep a seeded time before
+  // every claim; results must not change
+  uint32_t perturb;
 };
 
 // Bounded-wait records, one error word per code object (.hip file): take

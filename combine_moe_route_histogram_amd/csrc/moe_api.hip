@@ -114,7 +114,7 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 // Bound of the in-kernel waits, in ticks of the 100 MHz clock: 20 s, or
 // MOE_WAIT_LIMIT_US microseconds; MOE_DEBUG_UNREACHABLE_WAITS=1 adds one to
 // every wait's target (debug: exercises the timeout record).  Read at every
-// launch.
+// launch, as is MOE_DEBUG_PERTURB_SEED.
 void wait_bounds(GemmArgs& a) {
   a.wait_ticks = 20ull * 100000000ull;
   if (const char* e = getenv("MOE_WAIT_LIMIT_US")) {
@@ -124,6 +124,10 @@ void wait_bounds(GemmArgs& a) {
   }
   const char* u = getenv("MOE_DEBUG_UNREACHABLE_WAITS");
   a.wait_extra = (u && u[0] == '1') ? 1 : 0;
+  // MOE_DEBUG_PERTURB_SEED=n (n > 0): seeded claim order and delays in the
+  // persistent GEMM launches (debug: the results must not change)
+  a.perturb = 0;
+  if (const char* e = getenv("MOE_DEBUG_PERTURB_SEED")) a.perturb = (uint32_t)strtoul(e, nullptr, 10);
 }
 
 GemmArgs base_args(const moe_dims* d, const int32_t* offsets, void* ws) {

@@ -96,7 +96,11 @@ const char* moe_last_error(void);
  * The record is kept per device (the current one), not per stream: a wait
  * that gave up in work on another stream of the device is reported too.
  * Debug: MOE_DEBUG_UNREACHABLE_WAITS=1 in the environment at launch makes
- * every such wait target one more than can happen, to exercise this path. */
+ * every such wait target one more than can happen, to exercise this path.
+ * Debug: MOE_DEBUG_PERTURB_SEED=n (n > 0) at launch makes the persistent GEMM
+ * launches claim their whole tiles in a seeded order and sleep a seeded time
+ * before every claim; results are bit-identical to the normal schedule
+ * (slower; for determinism tests). */
 int moe_sync_status(void* stream);
 
 /* Bytes of device workspace the calls that take `ws` need for these dims
