@@ -26,6 +26,8 @@ SHAPES = [
     (64, 64, 4, 4, 64, 0),        # K = E
     (40, 128, 256, 8, 64, 1),     # 256 experts, most empty, a shared expert
     (2400, 64, 1, 1, 64, 1),      # groups of 10 row tiles: split into several bands
+    (33, 8, 4, 2, 8, 1),          # smallest H and I: one 16-byte vector per bf16 row
+    (50, 64, 4, 2, 64, 8),        # the maximum of 8 shared experts
 ]
 OUTS = ("dab", "dx_rows", "dw1", "dw3", "dw2", "dws1", "dws3", "dws2", "dx", "dtopk_w", "dlogits")
 

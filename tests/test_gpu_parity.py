@@ -31,6 +31,9 @@ SHAPES = [
     (150, 72, 4, 2, 88, 1),       # the same with a shared expert
     (2400, 64, 1, 1, 64, 1),      # groups of 10 row tiles: split into several bands
     (2200, 64, 2, 2, 64, 0),      # two experts of 2200 rows (9 row tiles) each
+    (33, 8, 4, 2, 8, 1),          # smallest H and I: one 16-byte vector per bf16 row
+    (20, 16, 3, 3, 24, 0),        # K = E, H and I below the vector count of a wave
+    (50, 64, 4, 2, 64, 8),        # the maximum of 8 shared experts (10 rows per token)
 ]
 
 
