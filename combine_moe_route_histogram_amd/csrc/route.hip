@@ -18,18 +18,25 @@ __global__ __launch_bounds__(64) void chunk_hist_kernel(const int32_t* __restric
                                   const int32_t* __restrict__ chunk_t0, int T, int E, int K,
                                   int32_t* __restrict__ chunk_counts);
 
-// Order-preserving 64-bit key: a larger logit gives a larger key; for equal
-// logits the lower expert id gives the larger key.  -0.0 is folded onto +0.0.
-__device__ __forceinline__ uint64_t route_key(float l, int e) {
+// Order-preserving 32-bit image of a finite logit (a larger logit gives a
+// larger value, never 0); -0.0 is folded onto +0.0.
+__device__ __forceinline__ uint32_t route_ord(float l) {
   uint32_t u = __float_as_uint(l);
   if ((u << 1) == 0u) u = 0u;
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float route_ord_logit(uint32_t hi) {
+  return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
+}
+
+// Order-preserving 64-bit key: a larger logit gives a larger key; for equal
+// logits the lower expert id gives the larger key.
+__device__ __forceinline__ uint64_t route_key(float l, int e) {
+  return ((uint64_t)route_ord(l) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
 __device__ __forceinline__ float route_key_logit(uint64_t key) {
-  const uint32_t hi = (uint32_t)(key >> 32);
-  return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
+  return route_ord_logit((uint32_t)(key >> 32));
 }
 
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
@@ -40,6 +47,11 @@ __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > 
 // each wave one group of 64 / G tokens, so a block takes 4 * 64 / G tokens:
 // the per-token rounds are short dependent shuffle chains, and many small
 // blocks keep enough of them in flight to hide their latency.
+//
+// E <= G (at most 64 experts: one expert per lane): the group maximum is
+// taken on the 32-bit order-preserving logit alone, and among the lanes that
+// hold it the lowest lane -- the lowest expert id -- wins (one ballot).  Same
+// selection, order and weights as the 64-bit keys, with half the shuffles.
 template <int G>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
                                                          int E, int K, int32_t* __restrict__ topk_idx,
@@ -49,6 +61,32 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   const int gl = lane & (G - 1), grp = lane / G;
   const int t = (blockIdx.x * 4 + wave) * TPW + grp;
   const bool valid = t < T;
+  if (E <= G) {
+    uint32_t v = (valid && gl < E) ? route_ord(logits[(int64_t)t * E + gl]) : 0u;   // 0: none
+    const uint64_t gmask = G == kWave ? ~0ull : (((1ull << (G % kWave)) - 1ull) << (grp * G));
+    float l0 = 0.f, zsum = 0.f, my_l = 0.f;
+    int my_e = 0;
+    for (int k = 0; k < K; ++k) {
+      uint32_t best = v;
+#pragma unroll
+      for (int o = G / 2; o >= 1; o >>= 1) best = max(best, (uint32_t)__shfl_xor((int)best, o, kWave));
+      const uint64_t cand = __ballot(v != 0u && v == best) & gmask;
+      const int e = __ffsll((unsigned long long)cand) - 1 - grp * G;   // lowest id among the ties
+      const float l = route_ord_logit(best);
+      if (gl == e) v = 0u;  // an expert is picked once
+      if (k == 0) l0 = l;
+      zsum += expf(l - l0);
+      if (gl == k) {
+        my_l = l;
+        my_e = e;
+      }
+    }
+    if (valid && gl < K) {
+      topk_idx[(int64_t)t * K + gl] = my_e;
+      topk_w[(int64_t)t * K + gl] = expf(my_l - l0) / zsum;
+    }
+    return;
+  }
   uint64_t key[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
