@@ -4,6 +4,8 @@
     python -m combine_moe_route_histogram_amd.profsum traffic --fetch D1 --write D2 \\
         --copy-fetch D3 --copy-write D4 --workload W --command-fetch C1 --command-write C2 \\
         --command-copy-fetch C3 --command-copy-write C4 --out BASE
+    python -m combine_moe_route_histogram_amd.profsum counters --mfma D1 --l2 D2 --title T \\
+        --command-mfma C1 --command-l2 C2 [--skip N] > OUT.md
 
 `stats` reads DIR/*kernel_stats.csv (rocprofv3 --kernel-trace --stats
 --output-format csv) and prints a Markdown table.  `traffic` reads the
@@ -13,7 +15,10 @@ the counter scale factors from the copy, and writes BASE.md (table) and
 BASE.json (per-kernel bytes per dispatch, plus a fingerprint of the kernel
 sources and build flags).  bench.py reports a kernel's traffic only while that
 fingerprint matches the sources it runs, so a kernel changed since its
-counters were taken reports none.
+counters were taken reports none.  `counters` reads a pass with
+GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES and SQ_INSTS_VALU_MFMA_MOPS_BF16
+and a pass with TCC_HIT_sum and TCC_MISS_sum, and prints per kernel the
+running clock, the MFMA busy share, the bf16 rate and the L2 hit rate.
 """
 from __future__ import annotations
 
@@ -197,6 +202,78 @@ def cmd_traffic(a):
     print(f"wrote {a.out}.json and {a.out}.md")
 
 
+# MI355X: GRBM_GUI_ACTIVE is collected per XCD and summed over the 8 XCDs;
+# SQ_VALU_MFMA_BUSY_CYCLES is counted per SIMD and summed over 256 CUs x 4
+# SIMDs.
+XCDS = 8
+SIMDS = 256 * 4
+
+
+def counter_runs(d: str, skip: int):
+    """Per kernel and counter: values of the dispatches after the first `skip`
+    (in dispatch order), and per kernel the dispatch durations in ns."""
+    vals = defaultdict(lambda: defaultdict(list))
+    with open(_one_csv(d, "counter_collection.csv")) as fh:
+        for r in csv.DictReader(fh):
+            k = short_name(r["Kernel_Name"])
+            vals[k][r["Counter_Name"]].append(
+                (int(r["Dispatch_Id"]), float(r["Counter_Value"]),
+                 int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    out = {}
+    for k, per in vals.items():
+        out[k] = {}
+        for c, v in per.items():
+            v.sort()
+            tail = v[skip:] or v
+            out[k][c] = ([x[1] for x in tail], [x[2] for x in tail])
+    return out
+
+
+def cmd_counters(a):
+    """MFMA utilisation at the running clock, the clock itself and the L2 hit
+    rate per kernel, from a pass with GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES
+    and SQ_INSTS_VALU_MFMA_MOPS_BF16 and a pass with TCC_HIT_sum and
+    TCC_MISS_sum."""
+    m = counter_runs(a.mfma, a.skip)
+    l2 = counter_runs(a.l2, a.skip)
+    mean = lambda xs: sum(xs) / len(xs)
+    rows = []
+    for k, c in m.items():
+        if "GRBM_GUI_ACTIVE" not in c or k.startswith("at::") or "elementwise" in k:
+            continue
+        gui, durs = c["GRBM_GUI_ACTIVE"]
+        ns = mean(durs)
+        cycles = mean(gui) / XCDS
+        busy = mean(c.get("SQ_VALU_MFMA_BUSY_CYCLES", ([0.0], []))[0])
+        mops = mean(c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", ([0.0], []))[0])
+        hit = miss = None
+        if k in l2 and "TCC_HIT_sum" in l2[k]:
+            hit, miss = mean(l2[k]["TCC_HIT_sum"][0]), mean(l2[k]["TCC_MISS_sum"][0])
+        rows.append((ns, k, len(durs), cycles / ns, busy / (SIMDS * cycles) if cycles else 0.0,
+                     mops * 512 / ns / 1e3, None if hit is None or hit + miss == 0 else hit / (hit + miss)))
+    rows.sort(reverse=True)
+    out = [f"# {a.title}", "", "Commands (from the repository root on an MI355X; one pass each):", "",
+           f"    {a.command_mfma}", f"    {a.command_l2}", ""]
+    if a.note:
+        out += [a.note, ""]
+    out += [f"Averages over the dispatches after the first {a.skip} of each kernel.  clock = "
+            f"GRBM_GUI_ACTIVE / {XCDS} (summed over the XCDs) / dispatch time; MFMA busy = "
+            f"SQ_VALU_MFMA_BUSY_CYCLES / ({SIMDS} SIMDs x clock cycles), the share of the matrix "
+            "cores' time at the running clock; bf16 TFLOP/s = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / "
+            "dispatch time (it counts the MFMAs issued, so rows of a partial 32-row block count "
+            "in full); L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS).  Dispatch times are under the "
+            "profiler; the clock is left out for dispatches under 100 us, whose busy window is "
+            "wider than their timestamps.", "",
+            "| kernel | dispatches | us | clock GHz | MFMA busy % | bf16 TFLOP/s | L2 hit % |",
+            "|---|---:|---:|---:|---:|---:|---:|"]
+    for ns, k, n, ghz, util, tf, l2h in rows:
+        l2s = "" if l2h is None else f"{100 * l2h:.1f}"
+        ghzs = f"{ghz:.2f}" if ns >= 100e3 else ""   # short dispatches: the busy window is wider
+        mf = (f"{100 * util:.1f}", f"{tf:.0f}") if tf > 0 else ("", "")
+        out.append(f"| {k} | {n} | {ns / 1e3:.1f} | {ghzs} | {mf[0]} | {mf[1]} | {l2s} |")
+    print("\n".join(out))
+
+
 def traffic_bytes(call: str, workload: str):
     """HBM bytes (read + written) per dispatch of the kernel behind `call`, from
     profiles/<workload>_hbm_traffic.json, or None if absent or taken on other
@@ -228,8 +305,13 @@ def main(argv=None):
     for n in ("fetch", "write", "copy-fetch", "copy-write", "workload", "out", "command-fetch",
               "command-write", "command-copy-fetch", "command-copy-write"):
         t.add_argument("--" + n, required=True)
+    c = sp.add_parser("counters")
+    for n in ("mfma", "l2", "title", "command-mfma", "command-l2"):
+        c.add_argument("--" + n, required=True)
+    c.add_argument("--note", default="")
+    c.add_argument("--skip", type=int, default=0, help="warm-up dispatches per kernel to leave out")
     a = ap.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":

@@ -61,3 +61,27 @@ def test_fingerprint_ignores_comments():
     b = "int f(int x) {\n  return x + 1;\n}\n"
     assert P._code_only(a) == P._code_only(b)
     assert P._code_only(a) != P._code_only(a.replace("+ 1", "+ 2"))
+
+
+def test_counters_clock_mfma_busy_and_l2_hit(tmp_path, capsys):
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    ns = 1_000_000                                   # 1 ms per dispatch
+    cycles = 1_600_000                               # 1.6 GHz per XCD
+    busy = 0.5 * P.SIMDS * cycles                    # matrix cores busy half the time
+    mfma, l2 = tmp_path / "mfma", tmp_path / "l2"
+    mfma.mkdir()
+    l2.mkdir()
+    rows = []
+    for i, scale in ((1, 3.0), (2, 1.0), (3, 1.0)):  # dispatch 1: warm-up, left out
+        for c, v in (("GRBM_GUI_ACTIVE", cycles * P.XCDS * scale), ("SQ_VALU_MFMA_BUSY_CYCLES", busy),
+                     ("SQ_INSTS_VALU_MFMA_MOPS_BF16", 1e12 / 512)):
+            rows.append([i, "void moe::gemm(int)", c, v, 0, ns])
+    _write(mfma / "p_counter_collection.csv", hdr, rows)
+    _write(l2 / "p_counter_collection.csv", hdr,
+           [[i, "void moe::gemm(int)", c, v, 0, ns] for i in (1, 2, 3)
+            for c, v in (("TCC_HIT_sum", 300.0), ("TCC_MISS_sum", 100.0))])
+    P.main(["counters", "--mfma", str(mfma), "--l2", str(l2), "--title", "T", "--command-mfma", "a",
+            "--command-l2", "b", "--skip", "1"])
+    row = [l for l in capsys.readouterr().out.splitlines() if l.startswith("| gemm ")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[1:] == ["2", "1000.0", "1.60", "50.0", "1000", "75.0"]
