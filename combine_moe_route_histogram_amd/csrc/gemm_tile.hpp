@@ -955,7 +955,7 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
 
 // ------------------------------------------------------------------ f32 ----
 
-constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16, kF32NT = 256;
+constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 64, kF32NT = 256;
 
 template <int KIND>
 __device__ void run_tile_f32(const GemmArgs& g, const TileDesc<float>& d, float* smem) {
@@ -970,16 +970,21 @@ __device__ void run_tile_f32(const GemmArgs& g, const TileDesc<float>& d, float*
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
   auto col_of = [&](int jj) { return PAIRED ? (jj < 2 ? 2 * tx + jj : 32 + 2 * tx + (jj - 2)) : 4 * tx + jj; };
-  for (int k0 = 0; k0 < d.k_len; k0 += kF32BK) {
+  // The next k step's operands are loaded into registers while the current
+  // step computes, and stored to LDS after its trailing barrier; every output
+  // still accumulates in ascending k.
+  constexpr int kLa = kF32BM * kF32BK / kF32NT, kLb = kF32BN * kF32BK / kF32NT;
+  float ra[kLa], rb[kLb];
+  auto load = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < kF32BM * kF32BK / kF32NT; ++i) {
+    for (int i = 0; i < kLa; ++i) {
       const int id = tid + i * kF32NT;
       const int m = id % kF32BM, k = id / kF32BM;
       const int kk = k0 + k;
-      sA[k][m] = (m < d.m_valid && kk < d.k_len) ? d.a[(int64_t)m * d.a_sm + (int64_t)kk * d.a_sk] : 0.f;
+      ra[i] = (m < d.m_valid && kk < d.k_len) ? d.a[(int64_t)m * d.a_sm + (int64_t)kk * d.a_sk] : 0.f;
     }
 #pragma unroll
-    for (int i = 0; i < kF32BN * kF32BK / kF32NT; ++i) {
+    for (int i = 0; i < kLb; ++i) {
       const int id = tid + i * kF32NT;
       const int n = id % kF32BN, k = id / kF32BN;
       int kk = k0 + k;
@@ -994,9 +999,23 @@ __device__ void run_tile_f32(const GemmArgs& g, const TileDesc<float>& d, float*
         kk -= d.ksplit;
       }
       const bool ok = nl < d.n_valid && (k0 + k) < d.k_len;
-      sB[k][n] = ok ? p[(int64_t)kk * d.b_sk + (int64_t)nl * d.b_sn] : 0.f;
+      rb[i] = ok ? p[(int64_t)kk * d.b_sk + (int64_t)nl * d.b_sn] : 0.f;
+    }
+  };
+  load(0);
+  for (int k0 = 0; k0 < d.k_len; k0 += kF32BK) {
+#pragma unroll
+    for (int i = 0; i < kLa; ++i) {
+      const int id = tid + i * kF32NT;
+      sA[id / kF32BM][id % kF32BM] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kLb; ++i) {
+      const int id = tid + i * kF32NT;
+      sB[id / kF32BN][id % kF32BN] = rb[i];
     }
     __syncthreads();
+    if (k0 + kF32BK < d.k_len) load(k0 + kF32BK);
 #pragma unroll
     for (int k = 0; k < kF32BK; ++k) {
       float av[4], bv[4];
