@@ -73,12 +73,14 @@ def copy_reference():
 
 
 def algorithmic_work(d, b):
-    """Algorithmic flop / byte counts per call (b = bytes per element)."""
+    """Algorithmic flop / byte counts per call (b = bytes per element).  Kinds:
+    "mfma" (flop), "hbm" (bytes; also timed with caches flushed), "latency"
+    (bytes, but a few small dependent launches: reported, not flushed)."""
     T, H, E, K, I, Ns, R = d.T, d.H, d.E, d.K, d.I, d.n_shared, d.R
     RA = R + Ns * T
     gemm = lambda rows, m: 2.0 * rows * H * I * m
     return {
-        "route": ("hbm", 4.0 * T * E + 8.0 * T * K + 4.0 * E + 8.0 * R),
+        "route": ("latency", 4.0 * T * E + 8.0 * T * K + 4.0 * E + 8.0 * R),
         "dispatch": ("hbm", b * T * H + b * R * H + 4.0 * R),
         "ffn_up": ("mfma", gemm(RA, 2)),
         "ffn_down": ("mfma", gemm(RA, 1)),
@@ -92,7 +94,7 @@ def algorithmic_work(d, b):
         "ffn_bwd_wgrad_down": ("mfma", gemm(RA, 1)),
         "ffn_bwd": ("mfma", gemm(RA, 6)),
         "dispatch_bwd": ("hbm", b * RA * H + b * T * H + 4.0 * R),
-        "route_bwd": ("hbm", 12.0 * T * K + 4.0 * T * E),
+        "route_bwd": ("latency", 12.0 * T * K + 4.0 * T * E),
     }
 
 
@@ -203,6 +205,8 @@ def main():
     hbm_flushed = {}
     if not args.no_hbm_flush:
         flush["buf"] = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        flush["buf"].fill_(1)   # first touch of the new buffer outside any timed call
+        torch.cuda.synchronize()
         step()
         torch.cuda.synchronize()
         flush["buf"] = None
