@@ -1,14 +1,21 @@
 """Throughput of the MoE expert layer (forward + backward) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
-                    [--unfused] [--no-cpu-baseline] [--cpu-tokens N]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload longseq]
+                    [--unfused] [--no-plain] [--no-cpu-baseline] [--cpu-tokens N]
 
 One step = one pass of the whole layer over one batch of synthetic, seeded
 inputs already resident in HBM: route (top-k, histogram, slot map) ->
 dispatch -> grouped SwiGLU GEMM -> down GEMM -> combine, then combine backward
 -> FFN input gradients -> FFN weight gradients -> dispatch backward -> gate
-backward.  Prints one JSON line.  Default workload: the Mixtral-like layer
-(T=4096 tokens, H=4096, E=8, top-2, I=14336, bf16).
+backward.  Prints one JSON line.  Default workload: the long-sequence slice
+(T=131072 tokens, H=2048, E=32, top-4, I=1408, bf16, forward + backward), the
+largest of the layer sizes that fits one GPU (the 128k-token workload of the
+UniEP article's evaluation).  The headline times the fused calls
+(dispatch+up, down+combine, the one-launch backward); the same run then times
+the plain calls over the same number of steps ("plain_path"), so fused and
+plain are compared on one GPU in one process.  After the timed steps the
+library's bounded-wait record is checked (moe_sync_status): a step in which
+a wait gave up is an error, not a result.
 
 Each library call inside the timed steps is bracketed by HIP events recorded
 on the stream the call launches on, so per-call device times are measured on
@@ -43,12 +50,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--workload", default="longseq")
     ap.add_argument("--unfused", action="store_true",
                     help="time the plain calls instead of the fused persistent kernels "
                          "(dispatch+up, down+combine, and the one-launch backward)")
+    ap.add_argument("--no-plain", action="store_true",
+                    help="do not time the plain calls after the fused ones")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=3072)
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens of the CPU-baseline sample (default: about 6e12 flop of oracle work)")
     ap.add_argument("--fwd-only", action="store_true")
     ap.add_argument("--no-hbm-flush", action="store_true",
                     help="skip the extra step that times the HBM-bound calls with the caches flushed")
@@ -118,6 +128,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    M.moe_init(0)
     cfg = synth.config(args.workload)
     if args.route_ranks:
         bench_route_ranks(args, cfg)
@@ -130,7 +141,6 @@ def main():
     d = L.make_dims(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.n_shared, cfg.dtype)
     b = L.Buffers(d, backward=backward)
     stream = torch.cuda.current_stream()
-    fused = not args.unfused
 
     calls = []  # (name, start_event, end_event)
     bpe = 2 if cfg.dtype == "bf16" else 4
@@ -147,7 +157,7 @@ def main():
         e1.record(stream)
         calls.append((name, e0, e1))
 
-    def step():
+    def step(fused):
         timed("route", L.route, b, p)
         if fused:
             timed("dispatch_ffn", M.moe_dispatch_ffn, d, p["x"], b.slot_src, b.slot, b.offsets, p["w1"],
@@ -181,34 +191,41 @@ def main():
             timed("dispatch_bwd", M.moe_dispatch_bwd, d, b.dx_rows, b.slot, b.dx)
             timed("route_bwd", M.moe_route_bwd, d, b.dtopk_w, b.topk_w, b.topk_idx, b.dlogits)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    calls.clear()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    tokens_per_s = cfg.T / (wall / args.steps)
+    def run(fused):
+        """W untimed steps, then exactly K timed steps between two device
+        synchronisations; returns (ms per step, mean device ms per call)."""
+        for _ in range(args.warmup):
+            step(fused)
+        torch.cuda.synchronize()
+        calls.clear()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(fused)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        # a bounded wait that gave up inside the timed steps makes them invalid
+        M.moe_sync_status()
+        per = {}
+        for name, e0, e1 in calls:
+            per.setdefault(name, []).append(e0.elapsed_time(e1))
+        calls.clear()
+        return wall * 1e3 / args.steps, {k: float(np.mean(v)) for k, v in per.items()}
 
-    per_call = {}
-    for name, e0, e1 in calls:
-        per_call.setdefault(name, []).append(e0.elapsed_time(e1))
-    per_call_ms = {k: float(np.mean(v)) for k, v in per_call.items()}
+    fused = not args.unfused
+    ms_per_step, per_call_ms = run(fused)
+    tokens_per_s = cfg.T / (ms_per_step * 1e-3)
 
     # one more step, untimed as a whole: a 512 MiB buffer is written before
     # each HBM-bound call, so its inputs come from HBM rather than from the
     # 256 MiB Infinity Cache (MALL) or L2, where the step leaves them
-    calls.clear()
     hbm_flushed = {}
     if not args.no_hbm_flush:
         flush["buf"] = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         flush["buf"].fill_(1)   # first touch of the new buffer outside any timed call
         torch.cuda.synchronize()
-        step()
+        step(fused)
         torch.cuda.synchronize()
+        M.moe_sync_status()
         flush["buf"] = None
     for name, e0, e1 in calls:
         kind, amount = work[name]
@@ -217,16 +234,30 @@ def main():
             rate = amount / (ms * 1e-3) / 1e9
             hbm_flushed[name] = {"ms": round(ms, 4), "GB/s": round(rate, 1),
                                  "frac": round(rate / PEAK_HBM_GBS, 4)}
-    breakdown = {}
-    for k, ms in per_call_ms.items():
-        kind, amount = work[k]
-        if kind == "mfma":
-            rate = amount / (ms * 1e-3) / 1e12
-            peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
-            breakdown[k] = {"ms": round(ms, 4), "TFLOP/s": round(rate, 1), "frac": round(rate / peak, 4)}
-        else:
-            rate = amount / (ms * 1e-3) / 1e9
-            breakdown[k] = {"ms": round(ms, 4), "GB/s": round(rate, 1), "frac": round(rate / PEAK_HBM_GBS, 4)}
+    calls.clear()
+
+    peak_mfma = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    def breakdown(per):
+        out = {}
+        for k, ms in per.items():
+            kind, amount = work[k]
+            if kind == "mfma":
+                rate = amount / (ms * 1e-3) / 1e12
+                out[k] = {"ms": round(ms, 4), "TFLOP/s": round(rate, 1), "frac": round(rate / peak_mfma, 4)}
+            else:
+                rate = amount / (ms * 1e-3) / 1e9
+                out[k] = {"ms": round(ms, 4), "GB/s": round(rate, 1), "frac": round(rate / PEAK_HBM_GBS, 4)}
+        return out
+
+    # the same number of steps of the other path, in the same process on the
+    # same buffers (fused vs plain on one GPU)
+    other = None
+    if not args.no_plain:
+        o_ms, o_per = run(not fused)
+        other = {"path": "unfused" if fused else "fused", "ms_per_step": round(o_ms, 4),
+                 "value": round(cfg.T / (o_ms * 1e-3), 1), "per_call": breakdown(o_per)}
+
     dom = max(per_call_ms, key=per_call_ms.get)
     kind, amount = work[dom]
     # HBM bytes per launch of the dominant kernel from the committed counter
@@ -234,10 +265,9 @@ def main():
     from combine_moe_route_histogram_amd.profsum import traffic_bytes
     traffic = traffic_bytes(dom, cfg.name)
     if kind == "mfma":
-        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
         ach = amount / (per_call_ms[dom] * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": peak_mfma,
+                    "unit": "TFLOP/s", "frac": round(ach / peak_mfma, 4), "traffic": traffic,
                     "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                     "work_per_launch": amount}
     else:
@@ -263,7 +293,8 @@ def main():
                    "path": "fused" if fused else "unfused"},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "per_call": breakdown,
+        "per_call": breakdown(per_call_ms),
+        "plain_path" if fused else "fused_path": other,
         "hbm_flushed": hbm_flushed,
         "input_gen_s": round(gen_s, 1),
     }
@@ -326,8 +357,21 @@ def bench_route_ranks(args, cfg):
     }), flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(cfg, inp, n_tokens, backward):
-    """The oracle as it stands, on the first n_tokens tokens with full weights."""
+    """The oracle as it stands, on the first n_tokens tokens with full weights
+    (default: about 6e12 flop of fp64 GEMM work, 10-30 s on a server CPU)."""
     import numpy as np
     import oracle as O
     try:
@@ -335,7 +379,10 @@ def cpu_baseline(cfg, inp, n_tokens, backward):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    n = min(n_tokens, cfg.T)
+    if n_tokens <= 0:
+        per_token = 2.0 * (cfg.K * cfg.I + cfg.n_shared * cfg.I_shared) * cfg.H * 3 * (3 if backward else 1)
+        n_tokens = int(6e12 / per_token)
+    n = max(1, min(n_tokens, cfg.T))
     sub = dict(inp)
     for k in ("logits", "x", "dout"):
         if k in sub:
@@ -347,7 +394,8 @@ def cpu_baseline(cfg, inp, n_tokens, backward):
     sec = time.perf_counter() - t0
     return {"value": round(n / sec, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {n} of {cfg.T} tokens, full expert weights, "
-                      f"{'fwd+bwd' if backward else 'fwd'}, fp64 numpy; {sec:.1f} s"}
+                      f"{'fwd+bwd' if backward else 'fwd'}, fp64 numpy; {sec:.1f} s",
+            "cpu": cpu_model(), "nproc": os.cpu_count()}
 
 
 if __name__ == "__main__":

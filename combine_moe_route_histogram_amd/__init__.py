@@ -35,9 +35,15 @@ def lib_path() -> str:
 
 
 class Dims(ctypes.Structure):
+    """moe_dims.  I_shared defaults to I when there are shared experts."""
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("I", ctypes.c_int32), ("n_shared", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("I_shared", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+    def __init__(self, T=0, H=0, E=0, K=0, I=0, n_shared=0, I_shared=None, dtype=BF16):
+        if I_shared is None:
+            I_shared = I if n_shared else 0
+        super().__init__(T, H, E, K, I, n_shared, I_shared, dtype)
 
     @property
     def R(self) -> int:

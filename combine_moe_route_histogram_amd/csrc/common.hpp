@@ -83,6 +83,37 @@ __device__ __forceinline__ int lane_int(int v, int k) { return __builtin_amdgcn_
 __device__ __forceinline__ float lane_float(float v, int k) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
 }
+// A token's K per-pair values (slot, gate weight, ...) spread over a wave:
+// lane l holds pairs l, l + 64, ... (NC chunks of 64: K <= 64 NC), loaded
+// while every lane is active.  at(k) reads pair k's value for a wave-uniform
+// k from whichever lane holds it.  The chunk is chosen AFTER the lane read,
+// among uniform values: at() is called inside loops where only some lanes
+// are active, and a per-lane select done there would leave the inactive
+// lanes' copies unwritten -- the very lanes a read of pair k may address.
+template <typename V, int NC>
+struct PairVals {
+  V v[NC];
+  __device__ __forceinline__ void load(const V* p, int K, int lane, V fill) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) v[c] = lane + kWave * c < K ? p[lane + kWave * c] : fill;
+  }
+  __device__ __forceinline__ static V read(V x, int l) {
+    if constexpr (__is_same(V, float)) return lane_float(x, l);
+    else return lane_int(x, l);
+  }
+  __device__ __forceinline__ V at(int k) const {
+    const int l = k & (kWave - 1);
+    V x = read(v[0], l);
+#pragma unroll
+    for (int c = 1; c < NC; ++c)
+      if (k >= kWave * c) x = read(v[c], l);
+    return x;
+  }
+};
+// Chunks of 64 pairs needed for K pairs per token (the kernels are
+// instantiated for 1 and 4, i.e. K <= 64 and K <= 256).
+inline int pair_chunks(int K) { return K <= kWave ? 1 : 4; }
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *static_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *static_cast<u32x4*>(p) = v; }
 

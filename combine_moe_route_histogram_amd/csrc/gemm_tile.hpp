@@ -14,15 +14,15 @@
 // runs in ascending k, so a tile's result does not depend on which worker
 // computes it or when.
 //
-// bf16 path: MFMA v_mfma_f32_32x32x16_bf16.  Both operands are staged in LDS
-// K-contiguous ([row][k], 64 k per row, 16-byte chunks XOR-swizzled by row
-// so that the 16-byte MFMA operand reads of 16 consecutive rows hit distinct
-// banks).  Operands that are K-contiguous in memory are copied with 16-byte
-// loads; operands that are MN-contiguous (weights in the forward, every
-// operand of the weight gradient) are read as 8(k) x 4(mn) blocks of 8-byte
-// loads and transposed in registers with v_perm before the LDS store.
-// Double-buffered LDS: the global loads of tile k+1 are in flight while the
-// MFMAs of tile k run.
+// bf16 path: MFMA v_mfma_f32_32x32x16_bf16.  Operands move global -> LDS
+// with buffer loads that write LDS directly (no register staging), each
+// operand in the layout it has in memory: K-contiguous operands as [row][64 k]
+// with 16-byte chunks XOR-swizzled by row, read back with ds_read_b128;
+// MN-contiguous operands (weights in the forward, both operands of the weight
+// gradient) as [k][columns] with a chunk XOR of 4 (k mod 4), read back with
+// the gfx950 LDS transpose read ds_read_b64_tr_b16, which hands each MFMA
+// lane its 8 consecutive k directly.  A ring of LDS k slices: the loads of
+// the next slice are in flight while the MFMAs of the current one run.
 //
 // f32 path: plain LDS-tiled FMA kernel (the MI355X fp32 vector and fp32
 // matrix peaks are equal, so VALU FMA loses nothing for fp32).

@@ -73,14 +73,18 @@ int check_dims(const moe_dims* d) {
   if (d->T < 1) return fail(MOE_EINVAL, "T must be >= 1 (got %d)", d->T);
   if (d->E < 1 || d->E > kMaxExperts)
     return fail(MOE_EUNSUPPORTED, "E must be in [1, %d] (got %d)", kMaxExperts, d->E);
-  if (d->K < 1 || d->K > d->E || d->K > 64)
-    return fail(MOE_EUNSUPPORTED, "K must be in [1, min(E, 64)] (got K=%d, E=%d)", d->K, d->E);
+  if (d->K < 1 || d->K > d->E)
+    return fail(MOE_EUNSUPPORTED, "K must be in [1, E] (got K=%d, E=%d)", d->K, d->E);
   if (d->H <= 0 || d->H % 8)
     return fail(MOE_EUNSUPPORTED, "H must be a positive multiple of 8 (got %d)", d->H);
   if (d->I <= 0 || d->I % 8)
     return fail(MOE_EUNSUPPORTED, "I must be a positive multiple of 8 (got %d)", d->I);
   if (d->n_shared < 0 || d->n_shared > 8)
     return fail(MOE_EUNSUPPORTED, "n_shared must be in [0, 8] (got %d)", d->n_shared);
+  if (d->n_shared > 0 && d->I_shared != d->I)
+    return fail(MOE_EUNSUPPORTED,
+                "shared experts must have the routed experts' intermediate dim (I_shared=%d, I=%d)",
+                d->I_shared, d->I);
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16)
     return fail(MOE_EUNSUPPORTED, "dtype must be MOE_F32 or MOE_BF16 (got %d)", d->dtype);
   const int64_t ra = (int64_t)d->T * d->K + (int64_t)d->n_shared * d->T;
@@ -111,23 +115,50 @@ int check_ws(const moe_dims* d, const void* ws, size_t ws_bytes) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-// Bound of the in-kernel waits, in ticks of the 100 MHz clock: 20 s, or
-// MOE_WAIT_LIMIT_US microseconds; MOE_DEBUG_UNREACHABLE_WAITS=1 adds one to
-// every wait's target (debug: exercises the timeout record).  Read at every
-// launch, as is MOE_DEBUG_PERTURB_SEED.
-void wait_bounds(GemmArgs& a) {
-  a.wait_ticks = 20ull * 100000000ull;
+// Debug settings, read from the environment by moe_init only (never at a
+// launch): the bound of the in-kernel waits in ticks of the 100 MHz clock
+// (20 s, or MOE_WAIT_LIMIT_US microseconds), MOE_DEBUG_UNREACHABLE_WAITS=1
+// (every wait's target one more than can happen: exercises the timeout
+// record), MOE_DEBUG_PERTURB_SEED=n (seeded claim order and delays in the
+// persistent GEMM launches; results must not change) and MOE_FUSED_WORKERS=n
+// (persistent workers of the fused calls; results must not change).
+struct DebugSettings {
+  uint64_t wait_ticks = 20ull * 100000000ull;
+  int wait_extra = 0;
+  uint32_t perturb = 0;
+  int fused_workers = 0;   // 0: one per CU
+};
+std::mutex g_debug_mu;
+DebugSettings g_debug;
+
+DebugSettings debug_settings() {
+  std::lock_guard<std::mutex> lk(g_debug_mu);
+  return g_debug;
+}
+
+void read_debug_settings() {
+  DebugSettings s;
   if (const char* e = getenv("MOE_WAIT_LIMIT_US")) {
     char* end = nullptr;
     const unsigned long long us = strtoull(e, &end, 10);
-    if (end != e) a.wait_ticks = us * 100ull;
+    if (end != e) s.wait_ticks = us * 100ull;
   }
   const char* u = getenv("MOE_DEBUG_UNREACHABLE_WAITS");
-  a.wait_extra = (u && u[0] == '1') ? 1 : 0;
-  // MOE_DEBUG_PERTURB_SEED=n (n > 0): seeded claim order and delays in the
-  // persistent GEMM launches (debug: the results must not change)
-  a.perturb = 0;
-  if (const char* e = getenv("MOE_DEBUG_PERTURB_SEED")) a.perturb = (uint32_t)strtoul(e, nullptr, 10);
+  s.wait_extra = (u && u[0] == '1') ? 1 : 0;
+  if (const char* e = getenv("MOE_DEBUG_PERTURB_SEED")) s.perturb = (uint32_t)strtoul(e, nullptr, 10);
+  if (const char* e = getenv("MOE_FUSED_WORKERS")) {
+    const int n = atoi(e);
+    s.fused_workers = n > 0 ? n : 0;
+  }
+  std::lock_guard<std::mutex> lk(g_debug_mu);
+  g_debug = s;
+}
+
+void wait_bounds(GemmArgs& a) {
+  const DebugSettings s = debug_settings();
+  a.wait_ticks = s.wait_ticks;
+  a.wait_extra = s.wait_extra;
+  a.perturb = s.perturb;
 }
 
 GemmArgs base_args(const moe_dims* d, const int32_t* offsets, void* ws) {
@@ -195,12 +226,10 @@ int fused_ws(const moe_dims* d, void* ws, FusedWs* w) {
   w->cursor = w->flags + L.mt_bound;
   w->mt_bound = L.mt_bound;
   MOE_TRY(current_cu_count(&w->workers));
-  // MOE_FUSED_WORKERS (debug): launch this many persistent workers instead,
-  // to check that results do not depend on how many workers share the tasks.
-  if (const char* e = getenv("MOE_FUSED_WORKERS")) {
-    const int n = atoi(e);
-    if (n > 0) w->workers = n;
-  }
+  // debug: this many persistent workers instead, to check that results do not
+  // depend on how many workers share the tasks
+  const int n = debug_settings().fused_workers;
+  if (n > 0) w->workers = n;
   return MOE_OK;
 }
 
@@ -210,6 +239,7 @@ extern "C" {
 
 int moe_init(int device) {
   if (device < 0 || device >= 64) return fail(MOE_EINVAL, "device index %d out of range", device);
+  read_debug_settings();
   std::lock_guard<std::mutex> lk(g_dev.mu);
   if (g_dev.cu_count[device]) return MOE_OK;
   int n = 0;
@@ -377,10 +407,10 @@ int moe_dispatch_ffn(const moe_dims* d, const void* x, const int32_t* slot_src,
   }
   MOE_TRY(check_ws(d, ws, ws_bytes));
   const hipStream_t st = as_stream(stream);
-  // f32 has no persistent kernel, and the bf16 one reads token rows with
-  // 32-bit byte offsets: otherwise a plain gather and the plain GEMM launch
-  // give the same result
-  if (d->dtype != MOE_BF16 || (int64_t)d->T * d->H * 2 > 0x7FFF0000LL) {
+  // f32 has no persistent kernel, the bf16 one reads token rows with 32-bit
+  // byte offsets and its copy tasks hold at most 64 pairs per token: otherwise
+  // a plain gather and the plain GEMM launch give the same result
+  if (d->dtype != MOE_BF16 || (int64_t)d->T * d->H * 2 > 0x7FFF0000LL || d->K > 64) {
     MOE_TRY(hip_status(launch_gather(d->dtype == MOE_BF16, x, slot_src, x_perm, d->T * d->K, d->H, st),
                        "moe_dispatch_ffn (gather)"));
     return moe_expert_ffn_up(d, x_perm, x, offsets, w1, w3, ws1, ws3, ab, h, ws, ws_bytes, stream);
@@ -407,8 +437,9 @@ int moe_ffn_combine(const moe_dims* d, const void* h, const int32_t* offsets, co
   if (d->n_shared) MOE_TRY(check_ptr(ws2, "ws2"));
   MOE_TRY(check_ws(d, ws, ws_bytes));
   const hipStream_t st = as_stream(stream);
-  if (d->dtype != MOE_BF16) {
-    // f32 has no persistent kernel: the two plain launches give the same result
+  if (d->dtype != MOE_BF16 || d->K > 64) {
+    // f32 has no persistent kernel, and the bf16 one's combine tasks hold at
+    // most 64 pairs per token: the two plain launches give the same result
     MOE_TRY(moe_expert_ffn_down(d, h, offsets, w2, ws2, y, ws, ws_bytes, stream));
     return moe_combine(d, y, slot, topk_w, out, stream);
   }

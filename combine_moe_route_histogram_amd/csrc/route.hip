@@ -93,8 +93,9 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     const int e = gl + i * G;
     key[i] = (valid && e < E) ? route_key(logits[(int64_t)t * E + e], e) : 0ull;
   }
-  float l0 = 0.f, zsum = 0.f, my_l = 0.f;
-  int my_e = 0;
+  // pick k is kept by lane k % 64 in slot k / 64 (K <= 256)
+  float l0 = 0.f, zsum = 0.f, my_l[4] = {0.f, 0.f, 0.f, 0.f};
+  int my_e[4] = {0, 0, 0, 0};
   for (int k = 0; k < K; ++k) {
     uint64_t best = umax64(umax64(key[0], key[1]), umax64(key[2], key[3]));
 #pragma unroll
@@ -109,14 +110,22 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
       if (e == gl + i * G) key[i] = 0ull;  // an expert is picked once
     if (k == 0) l0 = l;
     zsum += expf(l - l0);
-    if (gl == k) {
-      my_l = l;
-      my_e = e;
+    if (gl == (k & (G - 1))) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((k / G) == c) {
+          my_l[c] = l;
+          my_e[c] = e;
+        }
     }
   }
-  if (valid && gl < K) {
-    topk_idx[(int64_t)t * K + gl] = my_e;
-    topk_w[(int64_t)t * K + gl] = expf(my_l - l0) / zsum;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int k = gl + c * G;
+    if (valid && k < K) {
+      topk_idx[(int64_t)t * K + k] = my_e[c];
+      topk_w[(int64_t)t * K + k] = expf(my_l[c] - l0) / zsum;
+    }
   }
 }
 

@@ -28,14 +28,17 @@ __device__ __forceinline__ void st16_hint(void* p, const u32x4& v) {
 // dispatch backward).  NT: non-temporal loads and stores (plain launches,
 // whose rows stream through once); the fused kernel reads rows written by
 // other workgroups of the same launch and keeps ordinary loads.
-template <typename S, int U, int RB, bool NT>
+// NC: chunks of 64 pairs per token (K <= 64 NC).
+template <typename S, int U, int RB, bool NT, int NC = 1>
 __device__ __forceinline__ void combine_row(const S* __restrict__ y, const int32_t* __restrict__ slot,
                                             const float* __restrict__ w, S* __restrict__ out,
                                             int t, int T, int H, int K, int Ns, int lane) {
   constexpr int P = Elem<S>::kPerVec;
   const bool weighted = w != nullptr;
-  const int my_slot = lane < K ? slot[(int64_t)t * K + lane] : 0;
-  const float my_w = (weighted && lane < K) ? w[(int64_t)t * K + lane] : 0.f;
+  PairVals<int, NC> my_slot;
+  PairVals<float, NC> my_w;
+  my_slot.load(slot + (int64_t)t * K, K, lane, 0);
+  if (weighted) my_w.load(w + (int64_t)t * K, K, lane, 0.f);
   const int64_t R = (int64_t)T * K;
   const int nvec = H / P;
   const int nrows = K + Ns;
@@ -51,7 +54,7 @@ __device__ __forceinline__ void combine_row(const S* __restrict__ y, const int32
       for (int rb = 0; rb < RB; ++rb) {
         const int k = k0 + rb;
         if (k < nrows) {
-          const int64_t row = k < K ? (int64_t)lane_int(my_slot, k) : R + (int64_t)(k - K) * T + t;
+          const int64_t row = k < K ? (int64_t)my_slot.at(k) : R + (int64_t)(k - K) * T + t;
           const char* base = reinterpret_cast<const char*>(y + row * H);
 #pragma unroll
           for (int u = 0; u < U; ++u)   // a lane past the row's end reloads its last vector
@@ -62,7 +65,7 @@ __device__ __forceinline__ void combine_row(const S* __restrict__ y, const int32
       for (int rb = 0; rb < RB; ++rb) {
         const int k = k0 + rb;
         if (k < nrows) {
-          const float wk = lane_float(my_w, k < K ? k : 0);
+          const float wk = (weighted && k < K) ? my_w.at(k) : 0.f;
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             float f[P];
@@ -90,10 +93,11 @@ __device__ __forceinline__ void combine_row(const S* __restrict__ y, const int32
 // x_perm[slot[t,k]] = x[t] for k = 0..K-1: the token row is read once (U
 // 16-byte vectors per lane per round) and written to its K slots.  NT:
 // non-temporal loads (the plain launch, where nothing reads the row again).
-template <typename S, int U, bool NT>
+template <typename S, int U, bool NT, int NC = 1>
 __device__ __forceinline__ void dispatch_row(const S* __restrict__ x, const int32_t* __restrict__ slot,
                                              S* __restrict__ x_perm, int t, int H, int K, int lane) {
-  const int my_slot = lane < K ? slot[(int64_t)t * K + lane] : 0;
+  PairVals<int, NC> my_slot;
+  my_slot.load(slot + (int64_t)t * K, K, lane, 0);
   const int nvec = H / Elem<S>::kPerVec;
   const char* src = reinterpret_cast<const char*>(x + (int64_t)t * H);
   for (int v0 = lane; v0 < nvec; v0 += U * kWave) {
@@ -102,7 +106,7 @@ __device__ __forceinline__ void dispatch_row(const S* __restrict__ x, const int3
     for (int u = 0; u < U; ++u)   // a lane past the row's end reloads its last vector
       val[u] = ld16_hint<NT>(src + (int64_t)min(v0 + u * kWave, nvec - 1) * 16);
     for (int k = 0; k < K; ++k) {
-      char* dst = reinterpret_cast<char*>(x_perm + (int64_t)lane_int(my_slot, k) * H);
+      char* dst = reinterpret_cast<char*>(x_perm + (int64_t)my_slot.at(k) * H);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int v = v0 + u * kWave;

@@ -12,11 +12,12 @@ import torch
 from . import (BF16, F32, Dims, moe_combine, moe_combine_bwd, moe_dispatch, moe_dispatch_bwd,
                moe_dispatch_ffn, moe_expert_ffn_bwd, moe_expert_ffn_bwd_data, moe_expert_ffn_bwd_weight,
                moe_expert_ffn_down, moe_expert_ffn_up, moe_ffn_combine, moe_route, moe_route_bwd,
-               moe_workspace_bytes)
+               moe_sync_status, moe_workspace_bytes)
 
 
-def make_dims(T, H, E, K, I, n_shared=0, dtype="bf16") -> Dims:
-    return Dims(T, H, E, K, I, n_shared, BF16 if dtype == "bf16" else F32)
+def make_dims(T, H, E, K, I, n_shared=0, dtype="bf16", I_shared=None) -> Dims:
+    return Dims(T=T, H=H, E=E, K=K, I=I, n_shared=n_shared, I_shared=I_shared,
+                dtype=BF16 if dtype == "bf16" else F32)
 
 
 class Buffers:
@@ -95,3 +96,9 @@ def backward(b: Buffers, p: dict, fused: bool = False, stream=None):
                                   b.dw1, b.dw3, b.dw2, b.dws1, b.dws3, b.dws2, b.ws, stream)
     moe_dispatch_bwd(d, b.dx_rows, b.slot, b.dx, stream)
     moe_route_bwd(d, b.dtopk_w, b.topk_w, b.topk_idx, b.dlogits, stream)
+
+
+def check(stream=None):
+    """Wait for the step's work and raise MoeError (MOE_ETIMEOUT) if a bounded
+    wait inside a persistent kernel gave up, which leaves invalid results."""
+    moe_sync_status(stream)

@@ -23,7 +23,9 @@
  *    Router logits, gate weights, their gradients and weight gradients are
  *    always float32.  Indices and counts are int32.
  *  - Shapes: T tokens, H model dim, E routed experts, K experts per token,
- *    I expert intermediate dim, Ns = n_shared shared experts (same I).
+ *    I expert intermediate dim, Ns = n_shared shared experts of intermediate
+ *    dim I_shared (the kernels support I_shared == I; other values are
+ *    rejected with MOE_EUNSUPPORTED; ignored when Ns = 0).
  *    R = T*K routed rows.  "All rows" RA = R + Ns*T: rows [0, R) are the
  *    routed rows in slot order, rows [R + s*T, R + (s+1)*T) are shared
  *    expert s applied to tokens 0..T-1.
@@ -38,10 +40,10 @@
  *  - Every call returns a moe_status.  On error nothing has been launched
  *    and moe_last_error() gives a message (thread-local).
  *  - Validation (else MOE_EINVAL / MOE_EUNSUPPORTED): T >= 1,
- *    1 <= K <= E <= 256, K <= 64, H and I positive multiples of 8,
- *    0 <= Ns <= 8, R + Ns*T < 2^31; non-null pointers for every buffer the
- *    call uses.  Element offsets are computed in 64 bits, so buffers larger
- *    than 2^31 elements are fine.
+ *    1 <= K <= E <= 256, H and I positive multiples of 8, 0 <= Ns <= 8,
+ *    I_shared == I when Ns > 0, R + Ns*T < 2^31; non-null, 16-byte aligned
+ *    pointers for every buffer the call uses.  Element offsets are computed
+ *    in 64 bits, so buffers larger than 2^31 elements are fine.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -71,11 +73,17 @@ typedef struct {
   int32_t K;        /* experts per token (top-k)             */
   int32_t I;        /* expert FFN intermediate dim           */
   int32_t n_shared; /* shared experts (weight 1, all tokens) */
+  int32_t I_shared; /* shared experts' intermediate dim      */
   int32_t dtype;    /* moe_dtype                             */
 } moe_dims;
 
-/* Caches device properties (CU count) for `device`; idempotent.  Every other
- * call initialises lazily on the current device, so calling this is optional. */
+/* Caches device properties (CU count) for `device` and reads the debug
+ * settings listed under moe_sync_status from the environment.  No other call
+ * reads the environment: without moe_init the debug settings keep their
+ * defaults (waits bounded at 20 s, normal schedule, one persistent worker per
+ * CU), and every call initialises the device properties lazily.  May be
+ * called again (e.g. after changing a debug setting); the settings are global
+ * to the process.  Returns MOE_EINVAL for a device index outside [0, 64). */
 int moe_init(int device);
 
 /* Human-readable name of a status code; never NULL. */
@@ -89,18 +97,23 @@ const char* moe_last_error(void);
  * tasks on their row tiles, split-tail owners on their helpers, the
  * one-launch backward on its first phase) always end by construction; each
  * is also bounded in time (20 s, or MOE_WAIT_LIMIT_US microseconds from the
- * environment, read at launch), and one that gives up records it on the
- * device and lets the kernel run to its end with invalid results.
+ * environment as moe_init read it), and one that gives up records it on the
+ * device and lets the kernel run to its end with invalid results.  Callers
+ * that need valid results check this after their work (a timed-out step must
+ * not be reported as a result).
  * Returns MOE_ETIMEOUT if any wait gave up since the last call (then clears
  * the record), MOE_EHIP if the stream reports a HIP error, MOE_OK otherwise.
  * The record is kept per device (the current one), not per stream: a wait
  * that gave up in work on another stream of the device is reported too.
- * Debug: MOE_DEBUG_UNREACHABLE_WAITS=1 in the environment at launch makes
- * every such wait target one more than can happen, to exercise this path.
- * Debug: MOE_DEBUG_PERTURB_SEED=n (n > 0) at launch makes the persistent GEMM
- * launches claim their whole tiles in a seeded order and sleep a seeded time
- * before every claim; results are bit-identical to the normal schedule
- * (slower; for determinism tests). */
+ * Debug settings, read by moe_init only:
+ *  MOE_DEBUG_UNREACHABLE_WAITS=1 makes every such wait target one more than
+ *    can happen, to exercise this path;
+ *  MOE_DEBUG_PERTURB_SEED=n (n > 0) makes the persistent GEMM launches claim
+ *    their whole tiles in a seeded order and sleep a seeded time before every
+ *    claim; results are bit-identical to the normal schedule (slower; for
+ *    determinism tests);
+ *  MOE_FUSED_WORKERS=n (n > 0) launches n persistent workers in the fused
+ *    calls instead of one per CU (results do not depend on it). */
 int moe_sync_status(void* stream);
 
 /* Bytes of device workspace the calls that take `ws` need for these dims
@@ -191,9 +204,10 @@ int moe_combine(const moe_dims* d, const void* y, const int32_t* slot, const flo
  * and written to its K rows slot[t, 0..K-1].  slot_src [R] and slot [T, K]
  * are moe_route's outputs for the same routing.
  * Outputs (x_perm, ab, h) are bit-identical to moe_dispatch followed by
- * moe_expert_ffn_up.  f32, or bf16 with T*H*2 bytes above 2^31 - 64 KiB (the
- * kernel's per-lane byte offsets into x are 32-bit): a plain gather, then
- * moe_expert_ffn_up, with the same results. */
+ * moe_expert_ffn_up.  f32, bf16 with T*H*2 bytes above 2^31 - 64 KiB (the
+ * kernel's per-lane byte offsets into x are 32-bit), or K > 64 (its copy tasks
+ * hold at most 64 pairs per token): a plain gather, then moe_expert_ffn_up,
+ * with the same results. */
 int moe_dispatch_ffn(const moe_dims* d, const void* x, const int32_t* slot_src,
                      const int32_t* slot, const int32_t* offsets, const void* w1, const void* w3,
                      const void* ws1, const void* ws3, void* x_perm, void* ab, void* h, void* ws,
@@ -202,7 +216,7 @@ int moe_dispatch_ffn(const moe_dims* d, const void* x, const int32_t* slot_src,
 /* Fused GroupGEMM+Combine (UniEP section 2.1 second MegaKernel): the GEMM
  * tiles of moe_expert_ffn_down, then combine tasks that wait on per-row-tile
  * completion counters.  y and out are bit-identical to moe_expert_ffn_down
- * followed by moe_combine. */
+ * followed by moe_combine.  f32 or K > 64: those two plain launches. */
 int moe_ffn_combine(const moe_dims* d, const void* h, const int32_t* offsets, const void* w2,
                     const void* ws2, const int32_t* slot, const float* topk_w, void* y, void* out,
                     void* ws, size_t ws_bytes, void* stream);

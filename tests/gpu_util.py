@@ -1,10 +1,14 @@
 """Helpers of the GPU parity tests: device upload/download and the error
 measures of the parity bar (normwise relative error for bf16, max absolute
 error for f32)."""
+import contextlib
 import dataclasses
+import os
 
 import numpy as np
 import torch
+
+import combine_moe_route_histogram_amd as M
 
 import oracle as O
 import synth
@@ -57,3 +61,22 @@ def run_layer(cfg, inp, fused=False, backward=True):
         L.backward(b, p)
     torch.cuda.synchronize()
     return d, b
+
+
+@contextlib.contextmanager
+def debug_settings(**env):
+    """Run a block with the library's debug settings (environment variables
+    that moe_init reads; no other call reads the environment) set to `env`
+    (None: unset); they are unset and re-read afterwards."""
+    try:
+        for k, v in env.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = str(v)
+        M.moe_init(0)
+        yield
+    finally:
+        for k in env:
+            os.environ.pop(k, None)
+        M.moe_init(0)

@@ -65,7 +65,7 @@ def test_header_compiles_standalone(lang, tmp_path):
     if cc is None:
         pytest.skip("no host compiler")
     src = tmp_path / ("t.c" if lang == "c" else "t.cpp")
-    src.write_text('#include "moe.h"\nint main(void) { moe_dims d = {0}; return (int)sizeof(d) - 28; }\n')
+    src.write_text('#include "moe.h"\nint main(void) { moe_dims d = {0}; return (int)sizeof(d) - 32; }\n')
     r = subprocess.run([cc, "-Wall", "-Werror", "-fsyntax-only", "-I", os.path.dirname(HEADER), str(src)],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
@@ -86,8 +86,8 @@ def _dims(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(T=0), 1), (dict(E=0), 2), (dict(E=257), 2), (dict(K=0), 2), (dict(K=9), 2),
-    (dict(E=128, K=65), 2), (dict(H=100), 2), (dict(I=100), 2), (dict(n_shared=9), 2),
-    (dict(dtype=5), 2),
+    (dict(E=256, K=257), 2), (dict(H=100), 2), (dict(I=100), 2), (dict(n_shared=9), 2),
+    (dict(n_shared=1, I_shared=128), 2), (dict(n_shared=2, I_shared=0), 2), (dict(dtype=5), 2),
 ])
 def test_bad_dims_rejected_without_launch(lib, kw, status):
     d = _dims(**kw)
@@ -95,6 +95,26 @@ def test_bad_dims_rejected_without_launch(lib, kw, status):
     st = lib.moe_route(ctypes.byref(d), *([ctypes.c_void_p(16)] * 7), ctypes.c_void_p(256), 1 << 20, None)
     assert st == status
     assert M.moe_last_error() != ""
+
+
+@pytest.mark.parametrize("kw", [dict(E=256, K=256), dict(E=128, K=65), dict(n_shared=0, I_shared=77),
+                                dict(n_shared=3, I_shared=256)])
+def test_edge_dims_accepted(lib, kw):
+    """1 <= K <= E <= 256 with no other cap on K; I_shared is ignored
+    without shared experts and must equal I with them."""
+    d = _dims(**kw)
+    assert lib.moe_workspace_bytes(ctypes.byref(d)) > 0
+
+
+def test_dims_layout_matches_header():
+    """The binding's struct has the header's field order and size."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{(.*?)\} moe_dims;", src, flags=re.S).group(1)
+    fields = re.findall(r"int32_t\s+(\w+);", body)
+    assert fields == [f[0] for f in M.Dims._fields_]
+    assert ctypes.sizeof(M.Dims) == 4 * len(fields)
+    assert M.Dims(T=1, H=8, E=2, K=1, I=16, n_shared=1).I_shared == 16
+    assert M.Dims(T=1, H=8, E=2, K=1, I=16).I_shared == 0
 
 
 def test_null_misaligned_and_workspace_errors(lib):

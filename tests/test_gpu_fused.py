@@ -3,7 +3,6 @@ the same bits as the unfused launch sequence, whatever the number of
 persistent workers and on every rerun (the UniEP article's bit-consistency of
 the fused, overlapped execution with strictly sequential execution), and match
 the oracle like the unfused path."""
-import os
 
 import numpy as np
 import pytest
@@ -12,7 +11,7 @@ import torch
 import oracle as O
 import synth
 from combine_moe_route_histogram_amd import layer as L
-from gpu_util import custom_config, device_inputs, host, max_rel
+from gpu_util import custom_config, debug_settings, device_inputs, host, max_rel
 
 pytestmark = pytest.mark.gpu
 
@@ -33,11 +32,7 @@ OUTS = ("x_perm", "ab", "h", "y", "out")
 
 
 def _run(cfg, inp, fused, workers=None):
-    if workers is None:
-        os.environ.pop("MOE_FUSED_WORKERS", None)
-    else:
-        os.environ["MOE_FUSED_WORKERS"] = str(workers)
-    try:
+    with debug_settings(MOE_FUSED_WORKERS=workers):
         d = L.make_dims(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.n_shared, cfg.dtype)
         b = L.Buffers(d, backward=False)
         for t in (b.x_perm, b.ab, b.h, b.y, b.out):
@@ -45,8 +40,6 @@ def _run(cfg, inp, fused, workers=None):
         L.forward(b, device_inputs(inp), fused=fused)
         torch.cuda.synchronize()
         return b
-    finally:
-        os.environ.pop("MOE_FUSED_WORKERS", None)
 
 
 def _inputs(shape, dtype, seed=0):

@@ -3,7 +3,6 @@
 the GraphPP article's zero-bubble B/W split) gives the same bits as the two
 plain calls, B then W, whatever the number of persistent workers and on every
 rerun, and matches the oracle like them."""
-import os
 
 import numpy as np
 import pytest
@@ -12,7 +11,7 @@ import torch
 import oracle as O
 import synth
 from combine_moe_route_histogram_amd import layer as L
-from gpu_util import custom_config, device_inputs, f32_rel, host, max_rel
+from gpu_util import custom_config, debug_settings, device_inputs, f32_rel, host, max_rel
 
 pytestmark = pytest.mark.gpu
 
@@ -43,11 +42,7 @@ def _inputs(shape, dtype, seed=0):
 
 
 def _run(cfg, inp, fused_bwd, workers=None):
-    if workers is None:
-        os.environ.pop("MOE_FUSED_WORKERS", None)
-    else:
-        os.environ["MOE_FUSED_WORKERS"] = str(workers)
-    try:
+    with debug_settings(MOE_FUSED_WORKERS=workers):
         d = L.make_dims(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.n_shared, cfg.dtype)
         p = device_inputs(inp)
         b = L.Buffers(d)
@@ -59,8 +54,6 @@ def _run(cfg, inp, fused_bwd, workers=None):
         L.backward(b, p, fused=fused_bwd)
         torch.cuda.synchronize()
         return b
-    finally:
-        os.environ.pop("MOE_FUSED_WORKERS", None)
 
 
 def _same(ref, got):

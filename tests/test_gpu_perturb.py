@@ -11,14 +11,13 @@ is that the fused, overlapped execution is bit-consistent with strictly
 sequential execution: every output must be bit-identical to the unperturbed
 run.
 """
-import os
 
 import pytest
 import torch
 
 import synth
 from combine_moe_route_histogram_amd import layer as L
-from gpu_util import custom_config, device_inputs
+from gpu_util import custom_config, debug_settings, device_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -32,13 +31,7 @@ OUTS = ("x_perm", "ab", "h", "y", "out", "dy", "dtopk_w", "dab", "dx_rows", "dx"
 
 
 def _run(cfg, inp, fused, seed=None, workers=None):
-    env = {"MOE_DEBUG_PERTURB_SEED": seed, "MOE_FUSED_WORKERS": workers}
-    try:
-        for k, v in env.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = str(v)
+    with debug_settings(MOE_DEBUG_PERTURB_SEED=seed, MOE_FUSED_WORKERS=workers):
         d = L.make_dims(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.n_shared, cfg.dtype)
         b = L.Buffers(d)
         p = device_inputs(inp)
@@ -46,9 +39,6 @@ def _run(cfg, inp, fused, seed=None, workers=None):
         L.backward(b, p, fused=fused)
         torch.cuda.synchronize()
         return b
-    finally:
-        for k in env:
-            os.environ.pop(k, None)
 
 
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "plain"])

@@ -3,8 +3,8 @@ construction; each is also bounded in time, and one that gives up is recorded
 on the device and reported by moe_sync_status as MOE_ETIMEOUT while the
 kernel still runs to its end.  The give-up path is forced from the host
 (MOE_DEBUG_UNREACHABLE_WAITS: every wait targets one more than can happen,
-MOE_WAIT_LIMIT_US=0: give up at once), so every kernel exits normally."""
-import os
+MOE_WAIT_LIMIT_US=0: give up at once; both read by moe_init), so every kernel
+exits normally."""
 
 import pytest
 import torch
@@ -12,7 +12,7 @@ import torch
 import synth
 import combine_moe_route_histogram_amd as M
 from combine_moe_route_histogram_amd import layer as L
-from gpu_util import custom_config, device_inputs
+from gpu_util import custom_config, debug_settings, device_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -31,15 +31,8 @@ def _step(b, p, fused):
     L.backward(b, p, fused=fused)
 
 
-@pytest.fixture
-def clean_env():
-    yield
-    os.environ.pop("MOE_DEBUG_UNREACHABLE_WAITS", None)
-    os.environ.pop("MOE_WAIT_LIMIT_US", None)
-
-
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "plain"])
-def test_forced_timeout_is_reported_then_cleared(fused, clean_env):
+def test_forced_timeout_is_reported_then_cleared(fused):
     print(f"case forced wait timeout fused={fused}", flush=True)
     d, p = _setup()
     b = L.Buffers(d)
@@ -47,16 +40,13 @@ def test_forced_timeout_is_reported_then_cleared(fused, clean_env):
     M.moe_sync_status()                      # a normal step records nothing
     ref = {n: getattr(b, n).clone() for n in OUTS}
 
-    os.environ["MOE_DEBUG_UNREACHABLE_WAITS"] = "1"
-    os.environ["MOE_WAIT_LIMIT_US"] = "0"
-    _step(b, p, fused)                       # kernels give up their waits and exit
-    with pytest.raises(M.MoeError) as err:
-        M.moe_sync_status()
-    assert err.value.status == 5             # MOE_ETIMEOUT
-    M.moe_sync_status()                      # the record was cleared
+    with debug_settings(MOE_DEBUG_UNREACHABLE_WAITS=1, MOE_WAIT_LIMIT_US=0):
+        _step(b, p, fused)                   # kernels give up their waits and exit
+        with pytest.raises(M.MoeError) as err:
+            M.moe_sync_status()
+        assert err.value.status == 5         # MOE_ETIMEOUT
+        M.moe_sync_status()                  # the record was cleared
 
-    os.environ.pop("MOE_DEBUG_UNREACHABLE_WAITS")
-    os.environ.pop("MOE_WAIT_LIMIT_US")
     _step(b, p, fused)
     M.moe_sync_status()
     for n, t in ref.items():

@@ -125,6 +125,46 @@ def test_golden_hand_worked_route_and_slots():
     assert slot_src.tolist() == [int(v) for v in g["slot_src"][0]]
 
 
+def test_golden_hand_worked_bf16_rounding_points():
+    """One token through the whole bf16 layer, worked by hand: pins where the
+    layer rounds (h from the unrounded a, b; y from the stored h; out rounded
+    once; dy stored; da, db from the saved a, b; dx_perm one rounding of the
+    two paths; dx from the stored dx_perm rows).  Moving any of these rounding
+    points changes at least one value (each alternative is worked out in the
+    fixture's comments)."""
+    g = _read_golden("bf16_rounding_T1_H2_E2_K2_I1.txt")
+    bf = lambda key, shape: O.store(np.array(g[key], dtype=np.float64).reshape(shape), "bf16")
+    inp = {"logits": np.array(g["logits"], dtype=np.float32).reshape(1, 2),
+           "x": bf("x", (1, 2)), "w1": bf("w1", (2, 2, 1)), "w3": bf("w3", (2, 2, 1)),
+           "w2": bf("w2", (2, 1, 2)), "dout": bf("dout", (1, 2))}
+    # every input is exactly representable in bf16
+    for k in ("x", "w1", "w3", "w2", "dout"):
+        assert np.array_equal(O.widen(inp[k], "bf16").ravel(), np.array(g[k]).ravel()), k
+    f = O.forward(inp, 2, "bf16")
+    b = O.backward(inp, f, "bf16")
+    wid = lambda a: O.widen(a, "bf16")
+    assert f["topk_idx"].tolist() == [[0, 1]]
+    assert np.allclose(f["topk_w"].ravel(), np.array(g["topk_w"]).ravel(), rtol=1e-7, atol=0)
+    assert f["slot"].tolist() == [[0, 1]]
+    # bf16 storage points: exact bit equality with the hand-worked values
+    assert np.array_equal(wid(f["ab"][:, 0]), np.array(g["a"]).ravel())
+    assert np.array_equal(wid(f["ab"][:, 1]), np.array(g["b"]).ravel())
+    assert np.array_equal(wid(f["h"][:, 0]), np.array(g["h"]).ravel())
+    assert np.array_equal(wid(f["y"]), np.array(g["y"]).reshape(2, 2))
+    assert np.array_equal(wid(f["out"]).ravel(), np.array(g["out"]).ravel())
+    assert np.array_equal(wid(b["dy"]), np.array(g["dy"]).reshape(2, 2))
+    assert np.array_equal(wid(b["dab"][:, 0]), np.array(g["da"]).ravel())
+    assert np.array_equal(wid(b["dab"][:, 1]), np.array(g["db"]).ravel())
+    assert np.array_equal(wid(b["dx_perm"]), np.array(g["dx_perm"]).reshape(2, 2))
+    assert np.array_equal(wid(b["dx"]).ravel(), np.array(g["dx"]).ravel())
+    # float32 gradients: fp64 sums of stored operands, one float32 rounding
+    assert np.array_equal(b["dtopk_w"].ravel(), np.array(g["dtopk_w"], np.float32).ravel())
+    assert np.array_equal(b["dw1"].reshape(2, 2), np.array(g["dw1"], np.float32).reshape(2, 2))
+    assert np.array_equal(b["dw3"].reshape(2, 2), np.array(g["dw3"], np.float32).reshape(2, 2))
+    assert np.array_equal(b["dw2"].reshape(2, 2), np.array(g["dw2"], np.float32).reshape(2, 2))
+    assert np.allclose(b["dlogits"].ravel(), np.array(g["dlogits"]).ravel(), rtol=2e-7, atol=0)
+
+
 # ---------------------------------------------------------------- slot map ---
 
 def _cursor_map(idx, E):
