@@ -65,6 +65,10 @@ def parse():
     ap.add_argument("--route-ranks", type=int, default=0, metavar="G",
                     help="instead of the layer, time Algorithm 1 with G explicit ranks "
                          "(moe_route_ranks) on the workload's routing, beside the oracle")
+    ap.add_argument("--tune-sweep", action="store_true",
+                    help="instead of the headline, time the fused step for every candidate value "
+                         "of each schedule knob (one knob at a time) beside the band model's "
+                         "prediction, and print one JSON line")
     ap.add_argument("--copy-reference", action="store_true",
                     help="only run a plain 256 MiB device copy three times (the reference that "
                          "calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -132,6 +136,9 @@ def main():
     cfg = synth.config(args.workload)
     if args.route_ranks:
         bench_route_ranks(args, cfg)
+        return
+    if args.tune_sweep:
+        tune_sweep(args, cfg)
         return
     backward = ("bwd" in cfg.passes) and not args.fwd_only
     t_gen = time.time()
@@ -299,6 +306,99 @@ def main():
         "input_gen_s": round(gen_s, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+TUNE_CANDIDATES = {
+    "band_up": (2, 4, 8, 16),
+    "band_act": (2, 4, 8, 16),
+    "small_group": (2, 4, 5, 8, 12, 16),
+    "band_wgrad_up": (2, 4, 8, 16),
+    "band_wgrad_down": (2, 4, 8, 16),
+    "combine_tokens": (8, 16, 32, 64),
+    "copy_tokens": (16, 32, 64, 128),
+}
+# the calls whose time each knob changes
+TUNE_CALLS = {
+    "band_up": ("dispatch_ffn",), "band_act": ("ffn_bwd",), "small_group": ("dispatch_ffn", "ffn_bwd"),
+    "band_wgrad_up": ("ffn_bwd",), "band_wgrad_down": ("ffn_bwd",), "combine_tokens": ("ffn_combine",),
+    "copy_tokens": ("dispatch_ffn",),
+}
+
+
+def tune_sweep(args, cfg):
+    """Every candidate of every schedule knob (one at a time, the others at
+    the library's choice), timed on the fused step; the band model's
+    prediction beside the measured time of the call the knob schedules."""
+    import numpy as np
+    import torch
+    import synth
+    import combine_moe_route_histogram_amd as M
+    from combine_moe_route_histogram_amd import layer as L
+
+    backward = "bwd" in cfg.passes
+    inp = synth.make_inputs(cfg, with_grad=backward)
+    p = {k: synth.to_torch(v, "cuda") for k, v in inp.items()}
+    d = L.make_dims(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.n_shared, cfg.dtype)
+    b = L.Buffers(d, backward=backward)
+    stream = torch.cuda.current_stream()
+    chosen = M.moe_get_tuning(d).as_dict()
+    calls = []
+
+    def timed(name, fn, *a):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn(*a)
+        e1.record(stream)
+        calls.append((name, e0, e1))
+
+    def step():
+        L.route(b, p)
+        timed("dispatch_ffn", M.moe_dispatch_ffn, d, p["x"], b.slot_src, b.slot, b.offsets, p["w1"],
+              p["w3"], p.get("ws1"), p.get("ws3"), b.x_perm, b.ab, b.h, b.ws)
+        timed("ffn_combine", M.moe_ffn_combine, d, b.h, b.offsets, p["w2"], p.get("ws2"), b.slot,
+              b.topk_w, b.y, b.out, b.ws)
+        if backward:
+            M.moe_combine_bwd(d, p["dout"], b.y, b.slot, b.topk_w, b.dy, b.dtopk_w)
+            timed("ffn_bwd", M.moe_expert_ffn_bwd, d, b.dy, p.get("dout"), b.offsets, p["w1"], p["w3"],
+                  p["w2"], p.get("ws1"), p.get("ws3"), p.get("ws2"), b.ab, b.x_perm, p["x"], b.h,
+                  b.dab, b.dx_rows, b.dw1, b.dw3, b.dw2, b.dws1, b.dws3, b.dws2, b.ws)
+
+    def measure(tune):
+        if tune:
+            os.environ["MOE_TUNE"] = tune
+        else:
+            os.environ.pop("MOE_TUNE", None)
+        M.moe_init(0)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        calls.clear()
+        for _ in range(args.steps):
+            step()
+        M.moe_sync_status()
+        per = {}
+        for name, e0, e1 in calls:
+            per.setdefault(name, []).append(e0.elapsed_time(e1))
+        return {k: round(float(np.median(v)), 4) for k, v in per.items()}
+
+    base = measure(None)
+    sweep = {}
+    for knob, values in TUNE_CANDIDATES.items():
+        rows = []
+        for v in values:
+            ms = measure(f"{knob}={v}")
+            key = [c for c in TUNE_CALLS[knob] if c in ms]
+            pred = M.moe_tuning_predict(d, knob, v)
+            rows.append({"value": v, "chosen": v == chosen[knob],
+                         "ms": round(sum(ms[c] for c in key), 4),
+                         "predicted_bytes_per_flop": round(pred, 7) if pred >= 0 else None})
+            print(f"# {cfg.name} {knob}={v}: {rows[-1]}", file=sys.stderr, flush=True)
+        best = min(rows, key=lambda r: r["ms"])
+        sweep[knob] = {"calls": TUNE_CALLS[knob], "chosen": chosen[knob], "measured_best": best["value"],
+                       "candidates": rows}
+    measure(None)
+    print(json.dumps({"workload": cfg.name, "steps": args.steps, "warmup": args.warmup,
+                      "chosen": chosen, "baseline_ms": base, "sweep": sweep}), flush=True)
 
 
 def bench_route_ranks(args, cfg):

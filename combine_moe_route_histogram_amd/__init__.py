@@ -21,7 +21,8 @@ __all__ = [
     "moe_ffn_combine", "moe_combine_bwd", "moe_expert_ffn_bwd_data",
     "moe_expert_ffn_bwd_weight", "moe_dispatch_bwd", "moe_route_bwd", "moe_expert_ffn_bwd_act",
     "moe_expert_ffn_bwd_input", "moe_expert_ffn_bwd_weight_gate_up", "moe_expert_ffn_bwd_weight_down",
-    "moe_expert_ffn_bwd", "moe_sync_status",
+    "moe_expert_ffn_bwd", "moe_sync_status", "Tuning", "moe_get_tuning",
+    "moe_tuning_predict",
 ]
 
 F32, BF16 = 0, 1
@@ -58,6 +59,17 @@ class Dims(ctypes.Structure):
         return _TORCH_DTYPE[self.dtype]
 
 
+class Tuning(ctypes.Structure):
+    """moe_tuning: the schedule knobs (band heights, fused task sizes)."""
+    _fields_ = [("band_up", ctypes.c_int32), ("band_act", ctypes.c_int32),
+                ("small_group", ctypes.c_int32), ("band_wgrad_up", ctypes.c_int32),
+                ("band_wgrad_down", ctypes.c_int32), ("combine_tokens", ctypes.c_int32),
+                ("copy_tokens", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {f: int(getattr(self, f)) for f, _ in self._fields_}
+
+
 class MoeError(RuntimeError):
     def __init__(self, status: int, name: str, detail: str):
         super().__init__(f"{name} failed: {moe_status_str(status)}: {detail}")
@@ -71,6 +83,8 @@ _SIGS = {
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_workspace_bytes": (ctypes.c_size_t, [_D]),
+    "moe_get_tuning": (ctypes.c_int, [_D, ctypes.POINTER(Tuning)]),
+    "moe_tuning_predict": (ctypes.c_double, [_D, ctypes.c_char_p, ctypes.c_int]),
     "moe_sync_status": (ctypes.c_int, [_P]),
     "moe_route": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_route_ranks_workspace_bytes": (ctypes.c_size_t, [_D, ctypes.c_int]),
@@ -138,6 +152,18 @@ def moe_sync_status(stream=None) -> None:
     """Wait for `stream`; raise MoeError (MOE_ETIMEOUT) if a bounded wait inside
     a kernel gave up since the last check, or on a HIP error."""
     _call("moe_sync_status", _stream(stream))
+
+
+def moe_get_tuning(d: Dims) -> Tuning:
+    """The schedule knobs the library uses for these dims."""
+    t = Tuning()
+    _call("moe_get_tuning", ctypes.byref(d), ctypes.byref(t))
+    return t
+
+
+def moe_tuning_predict(d: Dims, knob: str, value: int) -> float:
+    """The band model's predicted bytes beyond L2 per flop (negative: not modelled)."""
+    return float(load().moe_tuning_predict(ctypes.byref(d), knob.encode(), int(value)))
 
 
 def moe_workspace_bytes(d: Dims) -> int:

@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["route.hip", "rows.hip", "gemm.hip", "fused.hip", "bwd.hip", "moe_api.hip"]
+SOURCES = ["route.hip", "rows.hip", "gemm.hip", "fused.hip", "bwd.hip", "tuning.hip", "moe_api.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

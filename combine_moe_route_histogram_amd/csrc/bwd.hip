@@ -55,7 +55,7 @@ static_assert(BuCfg::BM == BdCfg::BM, "both data-gradient phases use one row-til
 
 template <bool R>
 __global__ __launch_bounds__(BuCfg::NT) __attribute__((amdgpu_waves_per_eu(BuCfg::NW / 4, BuCfg::NW / 4)))
-void ffn_bwd_kernel(GemmArgs g, FusedWs w) {
+void ffn_bwd_kernel(GemmArgs g, FusedWs w, int band_wg_down, int band_wg_up) {
   MOE_LDS_RING(BuCfg, ring);
   __shared__ int task_slot;
   const int n_mt = *g.n_mtiles;
@@ -90,7 +90,7 @@ void ffn_bwd_kernel(GemmArgs g, FusedWs w) {
   // phase 2: dW2
   for_tasks_xcd_ranges(cur + kXcds, mt_wd * nt_wd, 0, 1, &task_slot, [&](const TaskPart& tp) {
     int tm, tn;
-    band_order<kWgDown>(tp.L, mt_wd, nt_wd, tm, tn);
+    band_order(tp.L, mt_wd, nt_wd, band_wg_down, tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kWgDown, WdCfg::BM, WdCfg::BN>(g, tm, tn);
     if (!d.skip) run_tile_bf16<WdCfg, false, R>(g, d, ring, tp);
   }, g.perturb);
@@ -102,7 +102,7 @@ void ffn_bwd_kernel(GemmArgs g, FusedWs w) {
   for_tasks_xcd_ranges(cur + 2 * kXcds, n_mt * nt_bd, g.split_wr, (2 * g.I + BdCfg::BK - 1) / BdCfg::BK,
                        &task_slot, [&](const TaskPart& tp) {
     int tm, tn;
-    band_order_groups(tp.L, nt_bd, g.bands, g.n_mtiles[1], tm, tn);
+    band_order_groups(tp.L, nt_bd, g.bands2, g.n_mtiles[2], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kBwdDown, BdCfg::BM, BdCfg::BN>(g, tm, tn);
     if (!d.skip) run_tile_bf16<BdCfg, false, R>(g, d, ring, tp);
   }, g.perturb);
@@ -110,23 +110,24 @@ void ffn_bwd_kernel(GemmArgs g, FusedWs w) {
   // phase 4: dW1 | dW3
   for_tasks_xcd_ranges(cur + 3 * kXcds, mt_wu * nt_wu, 0, 1, &task_slot, [&](const TaskPart& tp) {
     int tm, tn;
-    band_order<kWgUp>(tp.L, mt_wu, nt_wu, tm, tn);
+    band_order(tp.L, mt_wu, nt_wu, band_wg_up, tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kWgUp, WuCfg::BM, WuCfg::BN>(g, tm, tn);
     if (!d.skip) run_tile_bf16<WuCfg, false, R>(g, d, ring, tp);
   }, g.perturb);
 }
 
-hipError_t launch_ffn_bwd(const GemmArgs& a0, const FusedWs& w, hipStream_t st) {
+hipError_t launch_ffn_bwd(const GemmArgs& a0, const Tuning& tu, const FusedWs& w, hipStream_t st) {
   GemmArgs a = a0;
   a.mtiles = w.mtiles;
   a.n_mtiles = w.n_mtiles;
-  a.bands = w.bands;
+  a.bands = w.bands;     // activation gradient: tuned bands
+  a.bands2 = w.bands2;   // input gradient: the fixed bands of its plain launch (split tails)
   a.mt_max = w.mt_bound;
-  // row tiles, bands, and every counter and cursor of the launch cleared
-  hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, BuCfg::BM, big_group_band(kBwdUp),
-                             w.mtiles, w.n_mtiles,
-                             nullptr, w.bands, w.flags,
-                             w.mt_bound + kFusedCursors + kXcds * kSplitWr, st);
+  // row tiles, both band tables, and every counter and cursor of the launch cleared
+  hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, BuCfg::BM, tu.small_group, tu.band_act,
+                             w.mtiles, w.n_mtiles, nullptr, w.bands, w.flags,
+                             w.mt_bound + kFusedCursors + kXcds * kSplitWr, st, w.bands2, kSplitSmall,
+                             split_kind_band(kBwdDown));
   if (e != hipSuccess) return e;
   const int64_t mt = mtile_bound(a.T, a.K, a.E, a.Ns, BuCfg::BM);
   const int64_t tiles = mt * gemm_ntiles<kBwdUp>(a.H, a.I, BuCfg::BN) +
@@ -137,9 +138,9 @@ hipError_t launch_ffn_bwd(const GemmArgs& a0, const FusedWs& w, hipStream_t st) 
                             gemm_ntiles<kWgUp>(a.H, a.I, WuCfg::BN);
   if (tiles > INT_MAX - 8) return hipErrorInvalidValue;
   if (ragged_k(a.H, a.I, BuCfg::BK))
-    ffn_bwd_kernel<true><<<w.workers, BuCfg::NT, 0, st>>>(a, w);
+    ffn_bwd_kernel<true><<<w.workers, BuCfg::NT, 0, st>>>(a, w, tu.band_wg_down, tu.band_wg_up);
   else
-    ffn_bwd_kernel<false><<<w.workers, BuCfg::NT, 0, st>>>(a, w);
+    ffn_bwd_kernel<false><<<w.workers, BuCfg::NT, 0, st>>>(a, w, tu.band_wg_down, tu.band_wg_up);
   return hipGetLastError();
 }
 

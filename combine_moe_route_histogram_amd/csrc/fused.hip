@@ -46,7 +46,6 @@ namespace moe {
 using UpCfg = BfPick<kUp>::C;
 using DownCfg = BfPick<kDown>::C;
 
-constexpr int kCopyTokens = 32;  // tokens per x_perm copy task
 
 template <bool R>
 __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
@@ -68,15 +67,15 @@ __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
   // phase 2: the permuted copy x_perm (an output the backward reads), token
   // by token as the plain dispatch does it: each token row is read once and
   // written to its K slots (a copy by destination row would read every token
-  // row K times).  Tasks of kCopyTokens tokens, one wave per token, fill the
+  // row K times).  Tasks of g.task_tokens tokens, one wave per token, fill the
   // workers that the tile tail leaves idle.
-  const int n_copy = (g.T + kCopyTokens - 1) / kCopyTokens;
+  const int n_copy = (g.T + g.task_tokens - 1) / g.task_tokens;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   for (;;) {
     const int task = claim_task(&w.cursor[0], &task_slot);
     if (task >= n_copy) break;
-    const int t1 = min(g.T, (task + 1) * kCopyTokens);
-    for (int t = task * kCopyTokens + wave; t < t1; t += C::NW)
+    const int t1 = min(g.T, (task + 1) * g.task_tokens);
+    for (int t = task * g.task_tokens + wave; t < t1; t += C::NW)
       dispatch_row<uint16_t, 4, false>(static_cast<const uint16_t*>(g.x), slot,
                                        static_cast<uint16_t*>(g.o_x_perm), t, g.H, g.K, lane);
   }
@@ -98,7 +97,6 @@ __device__ __forceinline__ int tile_of_row(int64_t row, const GemmArgs& g, const
   return first_tile[lo] + (int)((row - g.offsets[lo]) / bm);
 }
 
-constexpr int kCombineTokens = 16;  // tokens per combine task
 
 template <bool R>
 __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
@@ -109,7 +107,7 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
   MOE_LDS_RING(C, ring);
   __shared__ int task_slot;
   const int n_mt = *w.n_mtiles;
-  const int n_comb = (g.T + kCombineTokens - 1) / kCombineTokens;
+  const int n_comb = (g.T + g.task_tokens - 1) / g.task_tokens;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   // phase 1: GEMM tiles; each completed tile counts towards its row tile
   for_tasks_xcd_ranges(w.cursor + 1, n_mt * nt_count, g.split_wr, (g.I + C::BK - 1) / C::BK,
@@ -132,8 +130,8 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
   for (;;) {
     const int task = claim_task(&w.cursor[0], &task_slot);
     if (task >= n_comb) break;
-    const int t0 = task * kCombineTokens;
-    const int t1 = min(g.T, t0 + kCombineTokens);
+    const int t0 = task * g.task_tokens;
+    const int t1 = min(g.T, t0 + g.task_tokens);
     if (!all_done) {
       // wave 0: unless every tile is published, wait until the row tiles
       // holding the task's routed rows (q < K) and shared-expert rows (q >= K)
@@ -166,16 +164,16 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
   }
 }
 
-hipError_t launch_dispatch_ffn(const GemmArgs& a0, const int32_t* slot_src, const int32_t* slot,
-                               const FusedWs& w, hipStream_t st) {
+hipError_t launch_dispatch_ffn(const GemmArgs& a0, const Tuning& tu, const int32_t* slot_src,
+                               const int32_t* slot, const FusedWs& w, hipStream_t st) {
   GemmArgs a = a0;
   a.mtiles = w.mtiles;
   a.n_mtiles = w.n_mtiles;
   a.bands = w.bands;
   a.a_rows = slot_src;
-  hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, UpCfg::BM, big_group_band(kUp),
-                             w.mtiles, w.n_mtiles,
-                             w.first_tile, w.bands, w.flags,
+  a.task_tokens = tu.copy_tokens;
+  hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, UpCfg::BM, tu.small_group, tu.band_up,
+                             w.mtiles, w.n_mtiles, w.first_tile, w.bands, w.flags,
                              w.mt_bound + kFusedCursors + kXcds * kSplitWr, st);
   if (e != hipSuccess) return e;
   const int nt = gemm_ntiles<kUp>(a.H, a.I, UpCfg::BN);
@@ -186,16 +184,17 @@ hipError_t launch_dispatch_ffn(const GemmArgs& a0, const int32_t* slot_src, cons
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_combine(const GemmArgs& a0, const int32_t* slot, const float* topk_w,
-                              const FusedWs& w, hipStream_t st) {
+hipError_t launch_ffn_combine(const GemmArgs& a0, const Tuning& tu, const int32_t* slot,
+                              const float* topk_w, const FusedWs& w, hipStream_t st) {
   GemmArgs a = a0;
   a.mtiles = w.mtiles;
   a.n_mtiles = w.n_mtiles;
   a.bands = w.bands;
-  hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, DownCfg::BM, big_group_band(kDown),
-                             w.mtiles, w.n_mtiles,
-                             w.first_tile, w.bands, w.flags,
-                             w.mt_bound + kFusedCursors + kXcds * kSplitWr, st);
+  a.task_tokens = tu.combine_tokens;
+  // the down projection splits its tail tiles: fixed bands, as in the plain launch
+  hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, DownCfg::BM, kSplitSmall,
+                             split_kind_band(kDown), w.mtiles, w.n_mtiles, w.first_tile, w.bands,
+                             w.flags, w.mt_bound + kFusedCursors + kXcds * kSplitWr, st);
   if (e != hipSuccess) return e;
   const int nt = gemm_ntiles<kDown>(a.H, a.I, DownCfg::BN);
   if (ragged_k(a.H, a.I, DownCfg::BK))

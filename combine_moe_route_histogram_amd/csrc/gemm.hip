@@ -15,17 +15,20 @@ namespace moe {
 // Row-tile table: per group (E routed experts, then Ns shared experts over
 // all T tokens) ceil(rows / bm) entries {group, first row, rows, 0}, groups in
 // order; n_mtiles[0] = number of entries.  Band table: a group of at most
-// kBandM row tiles is one band, a larger one runs of `big` row tiles
+// `small` row tiles is one band, a larger one runs of `big` row tiles
 // (group_bands); bands[b] = first row tile of band b, bands[nb] =
-// n_mtiles[0], n_mtiles[1] = nb.  One wave: each lane owns a contiguous run of
-// groups, wave scans give every lane its first table indices.
+// n_mtiles[0], n_mtiles[1] = nb; bands2 (if not null) likewise with small2,
+// big2 and n_mtiles[2].  One wave: each lane owns a contiguous run of groups,
+// wave scans give every lane its first table indices.
 __global__ __launch_bounds__(64) void plan_mtiles_kernel(const int32_t* __restrict__ offsets, int E,
-                                                         int Ns, int T, int R, int bm, int big,
-                                                         int4* __restrict__ mtiles,
+                                                         int Ns, int T, int R, int bm, int small,
+                                                         int big, int4* __restrict__ mtiles,
                                                          int32_t* __restrict__ n_mtiles,
                                                          int32_t* __restrict__ first_tile,
                                                          int32_t* __restrict__ bands,
-                                                         int32_t* __restrict__ clear, int n_clear) {
+                                                         int32_t* __restrict__ bands2, int small2,
+                                                         int big2, int32_t* __restrict__ clear,
+                                                         int n_clear) {
   __shared__ int off_s[kMaxExperts + 1];
   const int lane = threadIdx.x;
   const int G = E + Ns;
@@ -42,47 +45,59 @@ __global__ __launch_bounds__(64) void plan_mtiles_kernel(const int32_t* __restri
       rows = T;
     }
   };
-  int mine = 0, mine_b = 0;
+  int mine = 0, mine_b = 0, mine_b2 = 0;
   for (int grp = g_begin; grp < g_end; ++grp) {
     int row0, rows;
     group_rows(grp, row0, rows);
     const int mt = (rows + bm - 1) / bm;
     mine += mt;
-    mine_b += group_bands(mt, big);
+    mine_b += group_bands(mt, small, big);
+    if (bands2) mine_b2 += group_bands(mt, small2, big2);
   }
-  int incl = mine, incl_b = mine_b;
+  int incl = mine, incl_b = mine_b, incl_b2 = mine_b2;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
     const int y = __shfl_up(incl, o, kWave);
     const int yb = __shfl_up(incl_b, o, kWave);
+    const int yb2 = __shfl_up(incl_b2, o, kWave);
     if (lane >= o) {
       incl += y;
       incl_b += yb;
+      incl_b2 += yb2;
     }
   }
-  int idx = incl - mine, bidx = incl_b - mine_b;
+  int idx = incl - mine, bidx = incl_b - mine_b, bidx2 = incl_b2 - mine_b2;
   for (int grp = g_begin; grp < g_end; ++grp) {
     int row0, rows;
     group_rows(grp, row0, rows);
     if (first_tile) first_tile[grp] = idx;
     const int mt = (rows + bm - 1) / bm;
-    const int step = mt <= kBandM ? kBandM : big;
+    const int step = mt <= small ? small : big;
     for (int c = 0; c < mt; c += step) bands[bidx++] = idx + c;
+    if (bands2) {
+      const int step2 = mt <= small2 ? small2 : big2;
+      for (int c = 0; c < mt; c += step2) bands2[bidx2++] = idx + c;
+    }
     for (int r = 0; r < rows; r += bm) mtiles[idx++] = make_int4(grp, row0 + r, min(bm, rows - r), 0);
   }
   if (lane == kWave - 1) {
     n_mtiles[0] = incl;
     n_mtiles[1] = incl_b;
     bands[incl_b] = incl;
+    if (bands2) {
+      n_mtiles[2] = incl_b2;
+      bands2[incl_b2] = incl;
+    }
   }
   for (int i = lane; i < n_clear; i += kWave) clear[i] = 0;
 }
 
-hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int bm, int big,
-                       int4* mtiles, int32_t* n_mtiles, int32_t* first_tile, int32_t* bands,
-                       int32_t* clear, int n_clear, hipStream_t st) {
-  plan_mtiles_kernel<<<1, 64, 0, st>>>(offsets, E, Ns, T, R, bm, big, mtiles, n_mtiles, first_tile,
-                                       bands, clear, n_clear);
+hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int bm, int small,
+                       int big, int4* mtiles, int32_t* n_mtiles, int32_t* first_tile,
+                       int32_t* bands, int32_t* clear, int n_clear, hipStream_t st,
+                       int32_t* bands2, int small2, int big2) {
+  plan_mtiles_kernel<<<1, 64, 0, st>>>(offsets, E, Ns, T, R, bm, small, big, mtiles, n_mtiles,
+                                       first_tile, bands, bands2, small2, big2, clear, n_clear);
   return hipGetLastError();
 }
 
@@ -111,7 +126,7 @@ void gemm_bf16_kernel(GemmArgs g, int mt_fixed, int nt_count, int32_t* cursors, 
                        [&](const TaskPart& tp) {
     int tm, tn;
     if constexpr (KindTraits<C::KIND>::kWgrad)
-      band_order<C::KIND>(tp.L, mt_count, nt_count, tm, tn);
+      band_order(tp.L, mt_count, nt_count, g.wg_band, tm, tn);
     else
       band_order_groups(tp.L, nt_count, g.bands, g.n_mtiles[1], tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, C::KIND, C::BM, C::BN>(g, tm, tn);
@@ -135,17 +150,23 @@ __global__ __launch_bounds__(kF32NT) void gemm_f32_kernel(GemmArgs g, int mt_cou
 }
 
 template <int KIND>
-static hipError_t launch_kind(bool is_bf16, GemmArgs a, int4* mtiles_ws, int32_t* n_ws,
-                              int32_t* bands_ws, int32_t* cursors, int workers, hipStream_t st) {
+static hipError_t launch_kind(bool is_bf16, GemmArgs a, const Tuning& tu, int4* mtiles_ws,
+                              int32_t* n_ws, int32_t* bands_ws, int32_t* cursors, int workers,
+                              hipStream_t st) {
   using C = typename BfPick<KIND>::C;
   const int BM = is_bf16 ? C::BM : kF32BM;
   const int BN = is_bf16 ? C::BN : kF32BN;
   int mt_count;
   if constexpr (!KindTraits<KIND>::kWgrad) {
-    // the tile cursors and, kFusedCursors - 1 ints on, the split counters
-    plan_mtiles_kernel<<<1, 64, 0, st>>>(a.offsets, a.E, a.Ns, a.T, a.R, BM, big_group_band(KIND),
-                                         mtiles_ws, n_ws, nullptr, bands_ws, cursors,
-                                         is_bf16 ? (kFusedCursors - 1) + kXcds * kSplitWr : 0);
+    // bands: fixed for the kinds with split tails, else the tuned heights
+    const int small = KindTraits<KIND>::kSplit ? kSplitSmall : tu.small_group;
+    const int big = KindTraits<KIND>::kSplit ? split_kind_band(KIND)
+                    : KIND == kUp ? tu.band_up : tu.band_act;
+    // clears the tile cursors and, kFusedCursors - 1 ints on, the split counters
+    const hipError_t e = launch_plan(a.offsets, a.E, a.Ns, a.T, a.R, BM, small, big, mtiles_ws, n_ws,
+                                     nullptr, bands_ws, cursors,
+                                     is_bf16 ? (kFusedCursors - 1) + kXcds * kSplitWr : 0, st);
+    if (e != hipSuccess) return e;
     a.mtiles = mtiles_ws;
     a.n_mtiles = n_ws;
     a.bands = bands_ws;
@@ -153,6 +174,7 @@ static hipError_t launch_kind(bool is_bf16, GemmArgs a, int4* mtiles_ws, int32_t
     a.mt_max = mt_count;
   } else {
     mt_count = (a.E + a.Ns) * wgrad_mtiles<KIND>(a.H, a.I, BM);
+    a.wg_band = KIND == kWgUp ? tu.band_wg_up : tu.band_wg_down;
     a.split_wr = 0;   // many tiles per launch: no tail split
     if (is_bf16) clear_i32_kernel<<<1, 64, 0, st>>>(cursors, kXcds);
   }
@@ -175,10 +197,10 @@ static hipError_t launch_kind(bool is_bf16, GemmArgs a, int4* mtiles_ws, int32_t
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(bool is_bf16, int kind, const GemmArgs& a, int4* mtiles_ws,
-                       int32_t* n_mtiles_ws, int32_t* bands_ws, int32_t* cursors, int workers,
-                       hipStream_t st) {
-#define MOE_KIND(K) launch_kind<K>(is_bf16, a, mtiles_ws, n_mtiles_ws, bands_ws, cursors, workers, st)
+hipError_t launch_gemm(bool is_bf16, int kind, const GemmArgs& a, const Tuning& tu,
+                       int4* mtiles_ws, int32_t* n_mtiles_ws, int32_t* bands_ws, int32_t* cursors,
+                       int workers, hipStream_t st) {
+#define MOE_KIND(K) launch_kind<K>(is_bf16, a, tu, mtiles_ws, n_mtiles_ws, bands_ws, cursors, workers, st)
   switch (kind) {
     case kUp: return MOE_KIND(kUp);
     case kDown: return MOE_KIND(kDown);

@@ -461,6 +461,27 @@ __device__ __forceinline__ void lds_barrier() {
   __shared__ __align__(16) uint8_t name##3[C::STAGES > 3 ? C::STAGE_BYTES : 16];    \
   uint8_t* const name[4] = {name##0, name##1, name##2, name##3}
 
+// Block (wm, wn) of the tile that wave `wave` computes.  Normally wm = wave /
+// WGN, wn = wave % WGN.  The waves of a workgroup run on the CU's four SIMDs in
+// turn (wave w on SIMD w % 4), so with the 2 x 4 layout the waves of one wn
+// share a SIMD pair; a tile with at most half of its columns valid (the last
+// column tile when N is an odd multiple of BN/2, e.g. I = 1408 for 256-wide
+// tiles) would then leave two SIMDs with no MFMA work and the other two with
+// two waves each.  Such a tile takes wm = wave % WGM, wn = wave / WGM instead,
+// so its active waves (wn < WGN/2) are one per SIMD.  Which wave computes a
+// block does not change the block's arithmetic.
+template <class C>
+__device__ __forceinline__ void wave_block(const TileDesc<uint16_t>& d, int wave, int& wm, int& wn) {
+  constexpr bool kCanSpread = !C::PAIRED && C::WGM == 2 && C::WGN == 4;
+  if (kCanSpread && d.n_valid <= C::BN / 2 && d.m_valid > C::BM / 2) {
+    wm = wave % C::WGM;
+    wn = wave / C::WGM;
+  } else {
+    wm = wave / C::WGN;
+    wn = wave % C::WGN;
+  }
+}
+
 // Epilogue of one tile.  Each wave owns a WM x WN block of the tile; it moves
 // its accumulators, 32 rows x 64 columns (two 32x32 blocks) at a time, through
 // its own LDS region (row pitch 72 floats so the scattered writes of the 32x32
@@ -528,7 +549,8 @@ __device__ __forceinline__ void epilogue_bf16(const GemmArgs& g, const TileDesc<
   static_assert(NJ % 2 == 0, "the region takes two 32-column blocks at a time");
   constexpr int kRps = C::STAGE_BYTES / kEpiRegionBytes;   // regions per LDS slice
   static_assert(kRps >= 1 && (C::NW + kRps - 1) / kRps <= C::STAGES, "epilogue regions fit in the slices");
-  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  int wm, wn;
+  wave_block<C>(d, wave, wm, wn);
   const int rs = wave / kRps;
   uint8_t* const rbase = rs == 0 ? stages[0] : rs == 1 ? stages[1] : rs == 2 ? stages[2] : stages[3];
   float* reg = reinterpret_cast<float*>(rbase + (wave - rs * kRps) * kEpiRegionBytes);
@@ -771,7 +793,8 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  int wm, wn;
+  wave_block<C>(d, wave, wm, wn);
 
   // the weight gradient's k range (an expert's rows) is not a whole number
   // of slices; kRaggedK: neither is H or I (multiples of 8, not of the slice)
@@ -1051,34 +1074,18 @@ __device__ void run_tile_f32(const GemmArgs& g, const TileDesc<float>& d, float*
 
 constexpr int kF32LdsFloats = kF32BK * (kF32BM + 4) + kF32BK * (kF32BN + 4);
 
-// Logical tile -> (row tile, column tile).  Row tiles are taken in bands of
-// kBandM (the forward and input-gradient kinds, over each group's row tiles)
-// or WgradBand<KIND> (the weight-gradient kinds' fixed grid, whose M tiles
-// are H blocks for dW1/dW3 and I blocks for dW2); inside a band the column
-// tiles advance slowest, so the tiles an XCD runs at the same time form a
-// band x (concurrent / band) block: each operand slice they load is shared
-// by several of them through L2.  The heights were chosen by measurement.
-constexpr int kBandM = 8;
-// Row-tile bands of the forward and input-gradient kinds: a group of at most
-// kBandM row tiles is one band (its weights are then read by one band only);
-// a larger group is cut into bands of big_group_band(kind) row tiles -- 4,
-// so the band's token rows stay in L2 across its column tiles, except for
-// the down projection, whose short k rows make its weights the larger
-// operand (measured: 4 is 3-5 % faster than 8 for the up projection and
-// both input-side backward GEMMs at 64 row tiles per expert, 3 % slower for
-// the down projection; a 5-row-tile expert split into bands of 4 and 1 reads
-// its weights twice and runs 6 % slower).
-__host__ __device__ constexpr int big_group_band(int kind) { return kind == kDown ? kBandM : 4; }
-__host__ __device__ inline int group_bands(int mt, int big) {
-  return mt <= 0 ? 0 : mt <= kBandM ? 1 : (mt + big - 1) / big;
+// Logical tile -> (row tile, column tile).  Row tiles are taken in bands (the
+// forward and input-gradient kinds: over each group's row tiles, from the
+// planner's band table; the weight-gradient kinds: over their fixed grid of
+// (group, M tile), whose M tiles are H blocks for dW1/dW3 and I blocks for
+// dW2, GemmArgs::wg_band high); inside a band the column tiles advance
+// slowest, so the tiles an XCD runs at the same time form a band x
+// (concurrent / band) block: each operand slice they load is shared by
+// several of them through L2.  The heights are schedule knobs (Tuning).
+__host__ __device__ inline int group_bands(int mt, int small, int big) {
+  return mt <= 0 ? 0 : mt <= small ? 1 : (mt + big - 1) / big;
 }
-template <int KIND>
-struct WgradBand {
-  static constexpr int value = KIND == kWgUp ? 4 : 8;
-};
-template <int KIND>
-__device__ __forceinline__ void band_order(int L, int mt_count, int nt_count, int& tm, int& tn) {
-  constexpr int kB = WgradBand<KIND>::value;
+__device__ __forceinline__ void band_order(int L, int mt_count, int nt_count, int kB, int& tm, int& tn) {
   const int band_tiles = kB * nt_count;
   const int band = L / band_tiles;
   const int rem = L - band * band_tiles;
@@ -1205,7 +1212,7 @@ __device__ __forceinline__ void for_tasks_xcd_ranges(int32_t* cursors, int n, in
 }
 
 // Logical tile -> (row tile, column tile) over the planner's bands (a group's
-// row tiles in runs of at most kBandM): bands in order, inside a band the
+// row tiles in runs): bands in order, inside a band the
 // column tiles advance slowest.  Tiles running at the same time on an XCD
 // then belong to one or two experts, so they share weight columns as well as
 // token rows through L2.

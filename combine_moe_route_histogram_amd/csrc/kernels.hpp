@@ -21,6 +21,7 @@ hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* topk_
                         int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* slot_src,
                         int32_t* chunk_counts, int32_t* chunk_base, hipStream_t st);
 
+
 // Row kernels; is_bf16 selects the storage type (bf16 or f32).
 hipError_t launch_dispatch(bool is_bf16, const void* x, const int32_t* slot, void* x_perm, int T,
                            int H, int K, hipStream_t st);
@@ -54,14 +55,38 @@ enum GemmKind : int {
   kWgDown = 5,   // dW2 = h^T dY
 };
 
+// Schedule knobs (the auto-tuning space): each changes which tiles run
+// together on an XCD or how the fused kernels cut their row tasks, never the
+// arithmetic of an output element, so every choice gives the same bits.  The
+// GEMM kinds whose tail tiles are split along k (down projection, input
+// gradient) keep fixed bands: their split tiles are the last ones of each
+// XCD range in tile order, so a different order would split other tiles.
+struct Tuning {
+  int band_up;         // row tiles per band of a large group: gate/up projection
+  int band_act;        // the same for the activation gradient
+  int small_group;     // groups of at most this many row tiles are one band (those two kinds)
+  int band_wg_up;      // H blocks per band: dW1/dW3
+  int band_wg_down;    // I blocks per band: dW2
+  int combine_tokens;  // tokens per combine task of the fused down+combine
+  int copy_tokens;     // tokens per x_perm copy task of the fused dispatch+up
+};
+
+// Fixed bands of the split kinds: groups of at most kSplitSmall row tiles are
+// one band, larger ones run in bands of split_kind_band(kind).
+constexpr int kSplitSmall = 8;
+__host__ __device__ constexpr int split_kind_band(int kind) { return kind == kDown ? 8 : 4; }
+
 struct GemmArgs {
   int T, H, E, K, I, Ns, R;
   const int32_t* offsets;  // [E+1] routed row ranges
   const int4* mtiles;      // per M-tile {group, first row (all-rows index), rows, 0}
-  const int32_t* n_mtiles; // [0] valid entries in mtiles, [1] number of bands
-  const int32_t* bands;    // [bands + 1] first M-tile of each band (group_bands: a group of at most
-                           // kBandM M-tiles is one band; the last entry is the M-tile count)
+  const int32_t* n_mtiles; // [0] valid entries in mtiles, [1] bands in `bands`, [2] in `bands2`
+  const int32_t* bands;    // [bands + 1] first M-tile of each band (the last entry is the M-tile count)
+  const int32_t* bands2;   // second band table over the same M-tiles (the one-launch backward's
+                           // input-gradient phase), or null
   int mt_max;              // host bound on the number of M-tiles
+  int wg_band;             // weight-gradient kinds: M tiles per band
+  int task_tokens;         // fused kernels: tokens per combine or copy task
   const void* x_perm;
   const void* x;
   const void* w1;
@@ -141,16 +166,19 @@ constexpr int kMinTileM = 64;
 // bf16: `workers` persistent workgroups take the tiles through the kXcds
 // cursors at `cursors` (cleared by the launch itself); f32: one workgroup per
 // tile.
-hipError_t launch_gemm(bool is_bf16, int kind, const GemmArgs& a, int4* mtiles_ws,
-                       int32_t* n_mtiles_ws, int32_t* bands_ws, int32_t* cursors, int workers,
-                       hipStream_t st);
+hipError_t launch_gemm(bool is_bf16, int kind, const GemmArgs& a, const Tuning& tu,
+                       int4* mtiles_ws, int32_t* n_mtiles_ws, int32_t* bands_ws, int32_t* cursors,
+                       int workers, hipStream_t st);
 
 // Row-tile planner (one wave): table of bm-row tiles per group, the first
-// table index of every group (if first_tile), and n_clear ints of `clear` set
+// table index of every group (if first_tile), the band table (a group of at
+// most `small` row tiles is one band, a larger one runs of `big`) and, if
+// bands2, a second one with (small2, big2), and n_clear ints of `clear` set
 // to zero (flags and cursors of the fused kernels).
-hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int bm, int big,
-                       int4* mtiles, int32_t* n_mtiles, int32_t* first_tile, int32_t* bands,
-                       int32_t* clear, int n_clear, hipStream_t st);
+hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int bm, int small,
+                       int big, int4* mtiles, int32_t* n_mtiles, int32_t* first_tile,
+                       int32_t* bands, int32_t* clear, int n_clear, hipStream_t st,
+                       int32_t* bands2 = nullptr, int small2 = 0, int big2 = 0);
 
 // Fused persistent kernels (bf16).  ws_* are workspace sections.
 // Task cursors of a fused launch: [0] the x_perm copy (dispatch_ffn) or combine
@@ -166,17 +194,18 @@ struct FusedWs {
   int32_t* n_mtiles;
   int32_t* first_tile;  // [E + Ns]
   int32_t* bands;       // [mt bound + 1]
+  int32_t* bands2;      // [mt bound + 1]
   int32_t* flags;       // [mt bound]: done counters of the row tiles (ffn_combine)
   int32_t* cursor;      // [kFusedCursors], right after the flags
   int mt_bound;
   int workers;          // persistent workgroups to launch
 };
-hipError_t launch_dispatch_ffn(const GemmArgs& a, const int32_t* slot_src, const int32_t* slot,
-                               const FusedWs& w, hipStream_t st);
-hipError_t launch_ffn_combine(const GemmArgs& a, const int32_t* slot, const float* topk_w,
-                              const FusedWs& w, hipStream_t st);
+hipError_t launch_dispatch_ffn(const GemmArgs& a, const Tuning& tu, const int32_t* slot_src,
+                               const int32_t* slot, const FusedWs& w, hipStream_t st);
+hipError_t launch_ffn_combine(const GemmArgs& a, const Tuning& tu, const int32_t* slot,
+                              const float* topk_w, const FusedWs& w, hipStream_t st);
 // Expert-FFN backward in one persistent launch (bwd.hip): activation-gradient
 // tiles, then dW2 tiles, then input-gradient tiles, then dW1/dW3 tiles.
-hipError_t launch_ffn_bwd(const GemmArgs& a, const FusedWs& w, hipStream_t st);
+hipError_t launch_ffn_bwd(const GemmArgs& a, const Tuning& tu, const FusedWs& w, hipStream_t st);
 
 }  // namespace moe

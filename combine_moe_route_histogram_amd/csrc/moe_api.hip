@@ -11,6 +11,7 @@
 
 #include "../../include/moe.h"
 #include "kernels.hpp"
+#include "tuning.hpp"
 
 using namespace moe;
 
@@ -38,7 +39,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace sections (byte offsets).
 struct Layout {
-  size_t chunk_counts, chunk_base, mtiles, n_mtiles, bands, first_tile, flags, split, total;
+  size_t chunk_counts, chunk_base, mtiles, n_mtiles, bands, bands2, first_tile, flags, split, total;
   int mt_bound;
 };
 
@@ -52,6 +53,7 @@ Layout layout(const moe_dims* d) {
   L.mtiles = off;       off = align_up(off + mt * 16);
   L.n_mtiles = off;     off = align_up(off + 16);
   L.bands = off;        off = align_up(off + (mt + 1) * 4);
+  L.bands2 = off;       off = align_up(off + (mt + 1) * 4);
   L.first_tile = off;   off = align_up(off + (size_t)(d->E + d->n_shared) * 4);
   // row-tile counters, then the task cursors, then the split counters
   L.flags = off;        off = align_up(off + (mt + kFusedCursors + kXcds * kSplitWr) * 4);
@@ -127,6 +129,7 @@ struct DebugSettings {
   int wait_extra = 0;
   uint32_t perturb = 0;
   int fused_workers = 0;   // 0: one per CU
+  moe_tuning tune = {0, 0, 0, 0, 0, 0, 0};   // MOE_TUNE overrides (0: the shape's choice)
 };
 std::mutex g_debug_mu;
 DebugSettings g_debug;
@@ -136,8 +139,42 @@ DebugSettings debug_settings() {
   return g_debug;
 }
 
-void read_debug_settings() {
+// MOE_TUNE="key=value,...": schedule-knob overrides (keys as in moe_tuning).
+// Returns false for a malformed string or a value outside the knob's range.
+bool parse_tune(const char* e, moe_tuning* t) {
+  *t = moe_tuning{0, 0, 0, 0, 0, 0, 0};
+  std::string s(e);
+  size_t pos = 0;
+  while (pos < s.size()) {
+    size_t end = s.find(',', pos);
+    if (end == std::string::npos) end = s.size();
+    const std::string item = s.substr(pos, end - pos);
+    pos = end + 1;
+    if (item.empty()) continue;
+    const size_t eq = item.find('=');
+    if (eq == std::string::npos) return false;
+    const std::string key = item.substr(0, eq);
+    char* stop = nullptr;
+    const long v = strtol(item.c_str() + eq + 1, &stop, 10);
+    if (stop == item.c_str() + eq + 1 || *stop) return false;
+    int32_t* slot = key == "band_up" ? &t->band_up : key == "band_act" ? &t->band_act
+                  : key == "small_group" ? &t->small_group : key == "band_wgrad_up" ? &t->band_wgrad_up
+                  : key == "band_wgrad_down" ? &t->band_wgrad_down
+                  : key == "combine_tokens" ? &t->combine_tokens
+                  : key == "copy_tokens" ? &t->copy_tokens : nullptr;
+    if (!slot) return false;
+    const bool tokens = slot == &t->combine_tokens || slot == &t->copy_tokens;
+    if (v < 1 || v > (tokens ? kMaxTaskTokens : kMaxBand)) return false;
+    *slot = (int32_t)v;
+  }
+  return true;
+}
+
+bool read_debug_settings() {
   DebugSettings s;
+  if (const char* e = getenv("MOE_TUNE")) {
+    if (!parse_tune(e, &s.tune)) return false;
+  }
   if (const char* e = getenv("MOE_WAIT_LIMIT_US")) {
     char* end = nullptr;
     const unsigned long long us = strtoull(e, &end, 10);
@@ -152,6 +189,26 @@ void read_debug_settings() {
   }
   std::lock_guard<std::mutex> lk(g_debug_mu);
   g_debug = s;
+  return true;
+}
+
+// The schedule knobs for these dims: the shape's choice (choose_tuning), then
+// any MOE_TUNE override.
+Tuning tuning_for(const moe_dims* d) {
+  moe_tuning t = choose_tuning(d->T, d->H, d->E, d->K, d->I, d->n_shared);
+  const moe_tuning o = debug_settings().tune;
+  if (o.band_up) t.band_up = o.band_up;
+  if (o.band_act) t.band_act = o.band_act;
+  if (o.small_group) t.small_group = o.small_group;
+  if (o.band_wgrad_up) t.band_wgrad_up = o.band_wgrad_up;
+  if (o.band_wgrad_down) t.band_wgrad_down = o.band_wgrad_down;
+  if (o.combine_tokens) t.combine_tokens = o.combine_tokens;
+  if (o.copy_tokens) t.copy_tokens = o.copy_tokens;
+  Tuning u;
+  u.band_up = t.band_up; u.band_act = t.band_act; u.small_group = t.small_group;
+  u.band_wg_up = t.band_wgrad_up; u.band_wg_down = t.band_wgrad_down;
+  u.combine_tokens = t.combine_tokens; u.copy_tokens = t.copy_tokens;
+  return u;
 }
 
 void wait_bounds(GemmArgs& a) {
@@ -186,7 +243,7 @@ int gemm(const moe_dims* d, int kind, const GemmArgs& a, void* ws, hipStream_t s
   int workers = 0;
   MOE_TRY(current_cu_count(&workers));
   int32_t* cursors = ws_at<int32_t>(ws, L.flags) + L.mt_bound + 1;
-  return hip_status(launch_gemm(d->dtype == MOE_BF16, kind, a, ws_at<int4>(ws, L.mtiles),
+  return hip_status(launch_gemm(d->dtype == MOE_BF16, kind, a, tuning_for(d), ws_at<int4>(ws, L.mtiles),
                                 ws_at<int32_t>(ws, L.n_mtiles), ws_at<int32_t>(ws, L.bands),
                                 cursors, workers, st),
                     what);
@@ -222,6 +279,7 @@ int fused_ws(const moe_dims* d, void* ws, FusedWs* w) {
   w->n_mtiles = ws_at<int32_t>(ws, L.n_mtiles);
   w->first_tile = ws_at<int32_t>(ws, L.first_tile);
   w->bands = ws_at<int32_t>(ws, L.bands);
+  w->bands2 = ws_at<int32_t>(ws, L.bands2);
   w->flags = ws_at<int32_t>(ws, L.flags);
   w->cursor = w->flags + L.mt_bound;
   w->mt_bound = L.mt_bound;
@@ -239,7 +297,10 @@ extern "C" {
 
 int moe_init(int device) {
   if (device < 0 || device >= 64) return fail(MOE_EINVAL, "device index %d out of range", device);
-  read_debug_settings();
+  if (!read_debug_settings())
+    return fail(MOE_EINVAL, "MOE_TUNE must be key=value[,key=value...] with keys band_up, band_act, "
+                "small_group, band_wgrad_up, band_wgrad_down (1..%d), combine_tokens, copy_tokens "
+                "(1..%d)", kMaxBand, kMaxTaskTokens);
   std::lock_guard<std::mutex> lk(g_dev.mu);
   if (g_dev.cu_count[device]) return MOE_OK;
   int n = 0;
@@ -262,6 +323,29 @@ const char* moe_status_str(int status) {
 }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int moe_get_tuning(const moe_dims* d, moe_tuning* out) {
+  MOE_TRY(check_dims(d));
+  if (!out) return fail(MOE_EINVAL, "out is NULL");
+  const Tuning u = tuning_for(d);
+  out->band_up = u.band_up; out->band_act = u.band_act; out->small_group = u.small_group;
+  out->band_wgrad_up = u.band_wg_up; out->band_wgrad_down = u.band_wg_down;
+  out->combine_tokens = u.combine_tokens; out->copy_tokens = u.copy_tokens;
+  return MOE_OK;
+}
+
+double moe_tuning_predict(const moe_dims* d, const char* knob, int value) {
+  if (check_dims(d) != MOE_OK || !knob || value < 1 || value > kMaxBand) return -1.0;
+  const Tuning u = tuning_for(d);
+  const std::string k(knob);
+  auto pred = [&](bool act, int band, int small) {
+    return predict_traffic(d->T, d->H, d->E, d->K, d->I, d->n_shared, act, band, small);
+  };
+  if (k == "band_up") return pred(false, value, u.small_group);
+  if (k == "band_act") return pred(true, value, u.small_group);
+  if (k == "small_group") return pred(false, u.band_up, value) + pred(true, u.band_act, value);
+  return -1.0;
+}
 
 size_t moe_workspace_bytes(const moe_dims* d) {
   if (check_dims(d) != MOE_OK) return 0;
@@ -420,7 +504,7 @@ int moe_dispatch_ffn(const moe_dims* d, const void* x, const int32_t* slot_src,
   a.o_ab = ab; a.o_h = h;
   FusedWs w;
   MOE_TRY(fused_ws(d, ws, &w));
-  return hip_status(launch_dispatch_ffn(a, slot_src, slot, w, st), "moe_dispatch_ffn");
+  return hip_status(launch_dispatch_ffn(a, tuning_for(d), slot_src, slot, w, st), "moe_dispatch_ffn");
 }
 
 int moe_ffn_combine(const moe_dims* d, const void* h, const int32_t* offsets, const void* w2,
@@ -447,7 +531,7 @@ int moe_ffn_combine(const moe_dims* d, const void* h, const int32_t* offsets, co
   a.h = h; a.w2 = w2; a.ws2 = ws2; a.o_y = y; a.o_out = out;
   FusedWs w;
   MOE_TRY(fused_ws(d, ws, &w));
-  return hip_status(launch_ffn_combine(a, slot, topk_w, w, st), "moe_ffn_combine");
+  return hip_status(launch_ffn_combine(a, tuning_for(d), slot, topk_w, w, st), "moe_ffn_combine");
 }
 
 int moe_combine_bwd(const moe_dims* d, const void* dout, const void* y, const int32_t* slot,
@@ -606,7 +690,7 @@ int moe_expert_ffn_bwd(const moe_dims* d, const void* dy, const void* dout,
   a.o_dw1 = dw1; a.o_dw3 = dw3; a.o_dw2 = dw2; a.o_dws1 = dws1; a.o_dws3 = dws3; a.o_dws2 = dws2;
   FusedWs w;
   MOE_TRY(fused_ws(d, ws, &w));
-  return hip_status(launch_ffn_bwd(a, w, as_stream(stream)), "moe_expert_ffn_bwd");
+  return hip_status(launch_ffn_bwd(a, tuning_for(d), w, as_stream(stream)), "moe_expert_ffn_bwd");
 }
 
 int moe_sync_status(void* stream) {

@@ -116,6 +116,39 @@ const char* moe_last_error(void);
  *    calls instead of one per CU (results do not depend on it). */
 int moe_sync_status(void* stream);
 
+/* Schedule knobs of the grouped GEMMs and fused kernels (the auto-tuning
+ * space; UniEP article, section 3 of its table of contents: optimisation
+ * space, analytical performance model).  None of them changes the arithmetic
+ * of any output element -- only which tiles run together and how the fused
+ * kernels cut their row tasks -- so every choice gives the same output bits.
+ * The down projection and the input gradient, whose tail tiles are split
+ * along k, keep fixed bands. */
+typedef struct {
+  int32_t band_up;         /* row tiles per band of a large group: gate/up projection */
+  int32_t band_act;        /* the same for the activation gradient                    */
+  int32_t small_group;     /* a group of at most this many row tiles is one band      */
+  int32_t band_wgrad_up;   /* H blocks per band of the dW1/dW3 GEMM                   */
+  int32_t band_wgrad_down; /* I blocks per band of the dW2 GEMM                       */
+  int32_t combine_tokens;  /* tokens per combine task of moe_ffn_combine              */
+  int32_t copy_tokens;     /* tokens per x_perm copy task of moe_dispatch_ffn          */
+} moe_tuning;
+
+/* The knobs every call with these dims uses: the library's choice for the
+ * shape (an analytical model of the operand traffic beyond L2 for the band
+ * heights; measured defaults for the others), with any override from the
+ * MOE_TUNE environment variable as moe_init read it ("key=value,..." with the
+ * field names above; band heights 1..64, task sizes 1..1024; moe_init returns
+ * MOE_EINVAL for anything else).  Errors: MOE_EINVAL (NULL), bad dims. */
+int moe_get_tuning(const moe_dims* d, moe_tuning* out);
+
+/* The band model's prediction behind moe_get_tuning: operand bytes fetched
+ * from beyond L2 per flop of the GEMM that `knob` schedules ("band_up": the
+ * gate/up projection, "band_act": the activation gradient, "small_group":
+ * both, summed) with the knob at `value` and the others as chosen.  Returns
+ * a negative value for other knobs (the model does not cover them), for bad
+ * dims or a value outside 1..64. */
+double moe_tuning_predict(const moe_dims* d, const char* knob, int value);
+
 /* Bytes of device workspace the calls that take `ws` need for these dims
  * (route scratch, tile tables, readiness flags, task cursors).  The same
  * workspace may be reused by consecutive calls on one stream; calls that

@@ -186,3 +186,54 @@ def test_route_ranks_arguments(lib):
     assert st == 3
     st = lib.moe_route_ranks(ctypes.byref(d), p, 4, None, p, p, p, p, p, p, 1 << 20, None)
     assert st == 1 and "rank_counts" in M.moe_last_error()
+
+
+def _tuning(d):
+    return M.moe_get_tuning(d).as_dict()
+
+
+def test_tuning_choice_is_valid_and_follows_the_traffic_model(lib):
+    """moe_get_tuning on the host: valid knobs for every workload, and the
+    band heights the knob sweep measured fastest on MI355X: at the
+    long-sequence size the token rows (a 512 MiB gather) come from HBM while
+    the re-read weights stay in the Infinity Cache, so bands of 2 row tiles
+    win for the gate/up projection; where the token rows fit in the cache
+    (DeepSeek-like) bands of 4; Mixtral-like groups of 4-5 row tiles stay one
+    band.  The prediction for bands of 2 at the long-sequence size is the
+    model's closed form: 1 pass over the rows, 0.3-cost weights."""
+    import synth
+    dims = {}
+    for n in ("tiny", "mixtral", "dsv3", "skewed", "longseq"):
+        c = synth.config(n)
+        dims[n] = M.Dims(T=c.T, H=c.H, E=c.E, K=c.K, I=c.I, n_shared=c.n_shared,
+                         dtype=M.BF16 if c.dtype == "bf16" else M.F32)
+        t = _tuning(dims[n])
+        assert all(1 <= t[k] <= 64 for k in ("band_up", "band_act", "small_group", "band_wgrad_up",
+                                              "band_wgrad_down")), (n, t)
+        assert 1 <= t["combine_tokens"] <= 1024 and 1 <= t["copy_tokens"] <= 1024
+    assert _tuning(dims["longseq"])["band_up"] == 2
+    assert _tuning(dims["longseq"])["band_act"] == 4
+    assert _tuning(dims["dsv3"])["band_up"] == 4
+    assert _tuning(dims["mixtral"])["small_group"] >= 5
+    pred = M.moe_tuning_predict(dims["longseq"], "band_up", 2)
+    assert abs(pred - (1.0 / (11 * 256) + 0.3 / (2 * 256))) < 1e-12
+    assert M.moe_tuning_predict(dims["longseq"], "copy_tokens", 16) < 0     # not modelled
+
+
+def test_tuning_override_read_by_moe_init(lib, monkeypatch):
+    """MOE_TUNE overrides the shape's choice once moe_init has read it; a
+    malformed value is refused with MOE_EINVAL."""
+    d = M.Dims(T=4096, H=2048, E=32, K=4, I=1408, dtype=M.BF16)
+    base = _tuning(d)
+    monkeypatch.setenv("MOE_TUNE", "band_up=2,combine_tokens=64")
+    lib.moe_init(0)                      # on a host without a GPU: the settings are read first
+    t = _tuning(d)
+    assert t["band_up"] == 2 and t["combine_tokens"] == 64
+    assert {k: v for k, v in t.items() if k not in ("band_up", "combine_tokens")} == \
+        {k: v for k, v in base.items() if k not in ("band_up", "combine_tokens")}
+    for bad in ("band_up=0", "band_up=65", "copy_tokens=2000", "nope=3", "band_up", "band_up=x"):
+        monkeypatch.setenv("MOE_TUNE", bad)
+        assert lib.moe_init(0) == 1, bad
+    monkeypatch.delenv("MOE_TUNE")
+    lib.moe_init(0)
+    assert _tuning(d) == base
