@@ -21,7 +21,7 @@ __all__ = [
     "moe_ffn_combine", "moe_combine_bwd", "moe_expert_ffn_bwd_data",
     "moe_expert_ffn_bwd_weight", "moe_dispatch_bwd", "moe_route_bwd", "moe_expert_ffn_bwd_act",
     "moe_expert_ffn_bwd_input", "moe_expert_ffn_bwd_weight_gate_up", "moe_expert_ffn_bwd_weight_down",
-    "moe_expert_ffn_bwd", "moe_sync_status", "Tuning", "moe_get_tuning",
+    "moe_expert_ffn_bwd", "moe_sync_status", "moe_route_noalloc", "Tuning", "moe_get_tuning",
     "moe_tuning_predict",
 ]
 
@@ -87,6 +87,7 @@ _SIGS = {
     "moe_tuning_predict": (ctypes.c_double, [_D, ctypes.c_char_p, ctypes.c_int]),
     "moe_sync_status": (ctypes.c_int, [_P]),
     "moe_route": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_route_noalloc": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_route_ranks_workspace_bytes": (ctypes.c_size_t, [_D, ctypes.c_int]),
     "moe_route_ranks": (ctypes.c_int, [_D, _P, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P,
                                        ctypes.c_size_t, _P]),
@@ -218,6 +219,16 @@ def moe_route(d: Dims, logits, topk_idx, topk_w, counts, offsets, slot, slot_src
           _ptr(counts, "counts", torch.int32, E), _ptr(offsets, "offsets", torch.int32, E + 1),
           _ptr(slot, "slot", torch.int32, T * K), _ptr(slot_src, "slot_src", torch.int32, R),
           wp, wn, _stream(stream))
+
+
+def moe_route_noalloc(d: Dims, logits, topk_idx, topk_w, counts, offsets, slot, slot_src,
+                      stream=None):
+    T, E, K, R = d.T, d.E, d.K, d.R
+    _call("moe_route_noalloc", ctypes.byref(d), _ptr(logits, "logits", torch.float32, T * E),
+          _ptr(topk_idx, "topk_idx", torch.int32, T * K), _ptr(topk_w, "topk_w", torch.float32, T * K),
+          _ptr(counts, "counts", torch.int32, E), _ptr(offsets, "offsets", torch.int32, E + 1),
+          _ptr(slot, "slot", torch.int32, T * K), _ptr(slot_src, "slot_src", torch.int32, R),
+          _stream(stream))
 
 
 def moe_route_ranks_workspace_bytes(d: Dims, G: int) -> int:

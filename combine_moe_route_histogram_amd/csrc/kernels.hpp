@@ -21,6 +21,18 @@ hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* topk_
                         int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* slot_src,
                         int32_t* chunk_counts, int32_t* chunk_base, hipStream_t st);
 
+// Fixed device scratch of the routing variant that allocates nothing (for
+// callers that cannot allocate): one array per device, 1 MiB, holding the
+// per-chunk expert counts and bases (route_nchunk(T) * E ints each).
+constexpr int64_t kRouteScratchInts = 1 << 18;
+inline bool route_scratch_fits(int T, int E) {
+  return 2 * (int64_t)route_nchunk(T) * E <= kRouteScratchInts;
+}
+// Device address of the scratch array on `device`, looked up once per device
+// (the device is made current for the lookup) and cached.
+hipError_t route_scratch_prepare(int device);
+// The cached address for the current device (looked up on first use).
+hipError_t route_scratch_current(int32_t** out);
 
 // Row kernels; is_bf16 selects the storage type (bf16 or f32).
 hipError_t launch_dispatch(bool is_bf16, const void* x, const int32_t* slot, void* x_perm, int T,

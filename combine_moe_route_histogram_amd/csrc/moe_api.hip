@@ -301,6 +301,8 @@ int moe_init(int device) {
     return fail(MOE_EINVAL, "MOE_TUNE must be key=value[,key=value...] with keys band_up, band_act, "
                 "small_group, band_wgrad_up, band_wgrad_down (1..%d), combine_tokens, copy_tokens "
                 "(1..%d)", kMaxBand, kMaxTaskTokens);
+  // device address of moe_route_noalloc's fixed scratch on this device
+  MOE_TRY(hip_status(route_scratch_prepare(device), "moe_init (route scratch)"));
   std::lock_guard<std::mutex> lk(g_dev.mu);
   if (g_dev.cu_count[device]) return MOE_OK;
   int n = 0;
@@ -369,6 +371,30 @@ int moe_route(const moe_dims* d, const float* logits, int32_t* topk_idx, float* 
                                  slot_src, ws_at<int32_t>(ws, L.chunk_counts),
                                  ws_at<int32_t>(ws, L.chunk_base), as_stream(stream)),
                     "moe_route");
+}
+
+int moe_route_noalloc(const moe_dims* d, const float* logits, int32_t* topk_idx, float* topk_w,
+                      int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* slot_src,
+                      void* stream) {
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_ptr(logits, "logits"));
+  MOE_TRY(check_ptr(topk_idx, "topk_idx"));
+  MOE_TRY(check_ptr(topk_w, "topk_w"));
+  MOE_TRY(check_ptr(counts, "counts"));
+  MOE_TRY(check_ptr(offsets, "offsets"));
+  MOE_TRY(check_ptr(slot, "slot"));
+  MOE_TRY(check_ptr(slot_src, "slot_src"));
+  if (!route_scratch_fits(d->T, d->E))
+    return fail(MOE_EUNSUPPORTED,
+                "moe_route_noalloc: ceil(T/64)*E = %lld exceeds the fixed scratch (%lld); "
+                "use moe_route with a workspace",
+                (long long)route_nchunk(d->T) * d->E, (long long)kRouteScratchInts / 2);
+  int32_t* sc = nullptr;
+  MOE_TRY(hip_status(route_scratch_current(&sc), "moe_route_noalloc (scratch address)"));
+  const size_t half = (size_t)route_nchunk(d->T) * d->E;
+  return hip_status(launch_route(logits, d->T, d->E, d->K, topk_idx, topk_w, counts, offsets, slot,
+                                 slot_src, sc, sc + half, as_stream(stream)),
+                    "moe_route_noalloc");
 }
 
 size_t moe_route_ranks_workspace_bytes(const moe_dims* d, int G) {

@@ -9,6 +9,8 @@
 // lower chunks for e (exactly the rank-major prefix of the article), and the
 // position inside a chunk is the pair's rank among the chunk's pairs routed to
 // e, taken with wave ballots in (token, k) order.  No atomic decides a slot.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -263,6 +265,55 @@ hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* topk_
   route_slot_kernel<<<nchunk, 64, 0, st>>>(topk_idx, counts, chunk_base, nullptr, T, E, K, offsets,
                                            slot, slot_src);
   return hipGetLastError();
+}
+
+// ------------------------------------------------- static scratch variant --
+//
+// The routing scratch of moe_route_noalloc: a file-scope device array, one per
+// device, so that the call allocates nothing.  In host code `scratch` names a
+// host-side stand-in, not the device array: the kernels get the address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and cached.  Every call on a device shares its array; nothing in it
+// needs to start at zero (each word the kernels read was written earlier in
+// the same call), and calls that overlap in time on one device race.
+static __device__ __align__(256) int32_t scratch[kRouteScratchInts];
+
+namespace {
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[64] = {};
+
+hipError_t lookup_scratch_locked(int device) {
+  if (g_scratch_ptr[device]) return hipSuccess;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  g_scratch_ptr[device] = static_cast<int32_t*>(p);
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t route_scratch_prepare(int device) {
+  if (device < 0 || device >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[device]) return hipSuccess;
+  int prev = 0;
+  hipError_t e = hipGetDevice(&prev);
+  if (e != hipSuccess) return e;
+  if (prev != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+  e = lookup_scratch_locked(device);
+  const hipError_t r = prev != device ? hipSetDevice(prev) : hipSuccess;
+  return e != hipSuccess ? e : r;
+}
+
+hipError_t route_scratch_current(int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  e = lookup_scratch_locked(dev);   // the current device is the one looked up
+  *out = g_scratch_ptr[dev];
+  return e;
 }
 
 // ---------------------------------------------------------------- G ranks --

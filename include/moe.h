@@ -173,6 +173,21 @@ int moe_route(const moe_dims* d, const float* logits, int32_t* topk_idx, float* 
               int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* slot_src,
               void* ws, size_t ws_bytes, void* stream);
 
+/* moe_route for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same outputs, bit for bit, with the routing scratch taken from a fixed
+ * 1 MiB device array of the library instead of a caller workspace.  The
+ * array exists once per device and lives until the process ends; moe_init
+ * looks up its address (else the first call on the device does).  Limit:
+ * ceil(T / 64) * E <= 131072 (e.g. T = 131072 tokens with E <= 64), else
+ * MOE_EUNSUPPORTED before anything is launched.  Calls that overlap in time on
+ * one device share the array and race: order them on one stream.  Allocates
+ * nothing, frees nothing, does not synchronise.  Arguments and errors as for
+ * moe_route otherwise. */
+int moe_route_noalloc(const moe_dims* d, const float* logits, int32_t* topk_idx, float* topk_w,
+                      int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* slot_src,
+                      void* stream);
+
 /* Algorithm 1 with G explicit ranks (UniEP section 2.2, "deterministic token
  * mapping"): rank r holds the contiguous tokens [floor(T r / G),
  * floor(T (r+1) / G)), 1 <= G <= T.  Every rank counts its own (token, k)

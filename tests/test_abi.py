@@ -188,6 +188,17 @@ def test_route_ranks_arguments(lib):
     assert st == 1 and "rank_counts" in M.moe_last_error()
 
 
+def test_noalloc_route_refuses_sizes_beyond_its_scratch(lib):
+    """moe_route_noalloc checks the fixed scratch's limit (ceil(T/64)*E <=
+    131072) before touching the device."""
+    p = ctypes.c_void_p(4096)
+    d = _dims(T=32769, E=256, K=2)
+    st = lib.moe_route_noalloc(ctypes.byref(d), p, p, p, p, p, p, p, None)
+    assert st == 2 and "fixed scratch" in M.moe_last_error()
+    st = lib.moe_route_noalloc(ctypes.byref(_dims()), None, p, p, p, p, p, p, None)
+    assert st == 1 and "logits" in M.moe_last_error()
+
+
 def _tuning(d):
     return M.moe_get_tuning(d).as_dict()
 
