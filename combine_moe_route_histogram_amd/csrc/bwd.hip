@@ -72,7 +72,7 @@ void ffn_bwd_kernel(GemmArgs g, FusedWs w, int band_wg_down, int band_wg_up) {
   int mine = 0;
   for_tasks_xcd_ranges(cur, n_mt * nt_bu, 0, 1, &task_slot, [&](const TaskPart& tp) {
     int tm, tn;
-    band_order_groups(tp.L, nt_bu, g.bands, g.n_mtiles[1], tm, tn);
+    band_order_groups(tp.L, nt_bu, g.bands, tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kBwdUp, BuCfg::BM, BuCfg::BN>(g, tm, tn);
     if (!d.skip) run_tile_bf16<BuCfg, false, R>(g, d, ring, tp);
     ++mine;
@@ -102,7 +102,7 @@ void ffn_bwd_kernel(GemmArgs g, FusedWs w, int band_wg_down, int band_wg_up) {
   for_tasks_xcd_ranges(cur + 2 * kXcds, n_mt * nt_bd, g.split_wr, (2 * g.I + BdCfg::BK - 1) / BdCfg::BK,
                        &task_slot, [&](const TaskPart& tp) {
     int tm, tn;
-    band_order_groups(tp.L, nt_bd, g.bands2, g.n_mtiles[2], tm, tn);
+    band_order_groups(tp.L, nt_bd, g.bands2, tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kBwdDown, BdCfg::BM, BdCfg::BN>(g, tm, tn);
     if (!d.skip) run_tile_bf16<BdCfg, false, R>(g, d, ring, tp);
   }, g.perturb);

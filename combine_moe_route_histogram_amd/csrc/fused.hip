@@ -60,7 +60,7 @@ __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
   for_tasks_xcd_ranges(w.cursor + 1, n_mt * nt_count, 0, 1,
                        &task_slot, [&](const TaskPart& tp) {
     int tm, tn;
-    band_order_groups(tp.L, nt_count, w.bands, w.n_mtiles[1], tm, tn);
+    band_order_groups(tp.L, nt_count, w.bands, tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kUp, C::BM, C::BN>(g, tm, tn);
     run_tile_bf16<C, false, R>(g, d, ring, tp);
   }, g.perturb);
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(DownCfg::NT) void ffn_combine_kernel(GemmArgs g,
   for_tasks_xcd_ranges(w.cursor + 1, n_mt * nt_count, g.split_wr, (g.I + C::BK - 1) / C::BK,
                        &task_slot, [&](const TaskPart& tp) {
     int tm, tn;
-    band_order_groups(tp.L, nt_count, w.bands, w.n_mtiles[1], tm, tn);
+    band_order_groups(tp.L, nt_count, w.bands, tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kDown, C::BM, C::BN>(g, tm, tn);
     run_tile_bf16<C, true, R>(g, d, ring, tp);
     if (tp.part == tp.parts - 1)   // the tile is complete

@@ -16,17 +16,18 @@ namespace moe {
 // all T tokens) ceil(rows / bm) entries {group, first row, rows, 0}, groups in
 // order; n_mtiles[0] = number of entries.  Band table: a group of at most
 // `small` row tiles is one band, a larger one runs of `big` row tiles
-// (group_bands); bands[b] = first row tile of band b, bands[nb] =
-// n_mtiles[0], n_mtiles[1] = nb; bands2 (if not null) likewise with small2,
-// big2 and n_mtiles[2].  One wave: each lane owns a contiguous run of groups,
-// wave scans give every lane its first table indices.
+// (group_bands); bands[tm] = {first row tile, row tiles} of the band holding
+// row tile tm (so a worker finds a tile's band with one load), n_mtiles[1] =
+// number of bands; bands2 (if not null) likewise with small2, big2 and
+// n_mtiles[2].  One wave: each lane owns a contiguous run of groups, wave
+// scans give every lane its first table indices.
 __global__ __launch_bounds__(64) void plan_mtiles_kernel(const int32_t* __restrict__ offsets, int E,
                                                          int Ns, int T, int R, int bm, int small,
                                                          int big, int4* __restrict__ mtiles,
                                                          int32_t* __restrict__ n_mtiles,
                                                          int32_t* __restrict__ first_tile,
-                                                         int32_t* __restrict__ bands,
-                                                         int32_t* __restrict__ bands2, int small2,
+                                                         int2* __restrict__ bands,
+                                                         int2* __restrict__ bands2, int small2,
                                                          int big2, int32_t* __restrict__ clear,
                                                          int n_clear) {
   __shared__ int off_s[kMaxExperts + 1];
@@ -73,29 +74,33 @@ __global__ __launch_bounds__(64) void plan_mtiles_kernel(const int32_t* __restri
     if (first_tile) first_tile[grp] = idx;
     const int mt = (rows + bm - 1) / bm;
     const int step = mt <= small ? small : big;
-    for (int c = 0; c < mt; c += step) bands[bidx++] = idx + c;
+    for (int c = 0; c < mt; c += step) {
+      const int h = min(step, mt - c);
+      for (int j = 0; j < h; ++j) bands[idx + c + j] = make_int2(idx + c, h);
+      ++bidx;
+    }
     if (bands2) {
       const int step2 = mt <= small2 ? small2 : big2;
-      for (int c = 0; c < mt; c += step2) bands2[bidx2++] = idx + c;
+      for (int c = 0; c < mt; c += step2) {
+        const int h = min(step2, mt - c);
+        for (int j = 0; j < h; ++j) bands2[idx + c + j] = make_int2(idx + c, h);
+        ++bidx2;
+      }
     }
     for (int r = 0; r < rows; r += bm) mtiles[idx++] = make_int4(grp, row0 + r, min(bm, rows - r), 0);
   }
   if (lane == kWave - 1) {
     n_mtiles[0] = incl;
-    n_mtiles[1] = incl_b;
-    bands[incl_b] = incl;
-    if (bands2) {
-      n_mtiles[2] = incl_b2;
-      bands2[incl_b2] = incl;
-    }
+    n_mtiles[1] = bidx;
+    if (bands2) n_mtiles[2] = bidx2;
   }
   for (int i = lane; i < n_clear; i += kWave) clear[i] = 0;
 }
 
 hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int bm, int small,
                        int big, int4* mtiles, int32_t* n_mtiles, int32_t* first_tile,
-                       int32_t* bands, int32_t* clear, int n_clear, hipStream_t st,
-                       int32_t* bands2, int small2, int big2) {
+                       int2* bands, int32_t* clear, int n_clear, hipStream_t st,
+                       int2* bands2, int small2, int big2) {
   plan_mtiles_kernel<<<1, 64, 0, st>>>(offsets, E, Ns, T, R, bm, small, big, mtiles, n_mtiles,
                                        first_tile, bands, bands2, small2, big2, clear, n_clear);
   return hipGetLastError();
@@ -128,7 +133,7 @@ void gemm_bf16_kernel(GemmArgs g, int mt_fixed, int nt_count, int32_t* cursors, 
     if constexpr (KindTraits<C::KIND>::kWgrad)
       band_order(tp.L, mt_count, nt_count, g.wg_band, tm, tn);
     else
-      band_order_groups(tp.L, nt_count, g.bands, g.n_mtiles[1], tm, tn);
+      band_order_groups(tp.L, nt_count, g.bands, tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, C::KIND, C::BM, C::BN>(g, tm, tn);
     if (!d.skip) run_tile_bf16<C, false, R>(g, d, ring, tp);
   }, g.perturb);
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(kF32NT) void gemm_f32_kernel(GemmArgs g, int mt_cou
 
 template <int KIND>
 static hipError_t launch_kind(bool is_bf16, GemmArgs a, const Tuning& tu, int4* mtiles_ws,
-                              int32_t* n_ws, int32_t* bands_ws, int32_t* cursors, int workers,
+                              int32_t* n_ws, int2* bands_ws, int32_t* cursors, int workers,
                               hipStream_t st) {
   using C = typename BfPick<KIND>::C;
   const int BM = is_bf16 ? C::BM : kF32BM;
@@ -198,7 +203,7 @@ static hipError_t launch_kind(bool is_bf16, GemmArgs a, const Tuning& tu, int4* 
 }
 
 hipError_t launch_gemm(bool is_bf16, int kind, const GemmArgs& a, const Tuning& tu,
-                       int4* mtiles_ws, int32_t* n_mtiles_ws, int32_t* bands_ws, int32_t* cursors,
+                       int4* mtiles_ws, int32_t* n_mtiles_ws, int2* bands_ws, int32_t* cursors,
                        int workers, hipStream_t st) {
 #define MOE_KIND(K) launch_kind<K>(is_bf16, a, tu, mtiles_ws, n_mtiles_ws, bands_ws, cursors, workers, st)
   switch (kind) {

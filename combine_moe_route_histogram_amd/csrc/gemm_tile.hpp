@@ -532,7 +532,15 @@ __device__ __forceinline__ void ld_bf16x4(const void* p, float* v) {
   v[0] = __uint_as_float(w[0] << 16); v[1] = __uint_as_float(w[0] & 0xFFFF0000u);
   v[2] = __uint_as_float(w[1] << 16); v[3] = __uint_as_float(w[1] & 0xFFFF0000u);
 }
-__device__ __forceinline__ float fast_sigmoid(float a) { return __frcp_rn(1.0f + __expf(-a)); }
+// sigmoid(a) = 1 / (1 + e^-a) with the hardware exponential and reciprocal
+// (v_exp_f32, v_rcp_f32: about 1 ulp each; the argument of the reciprocal is
+// >= 1, so no denormal or overflow case: e^-a = inf gives 0).  A correctly
+// rounded reciprocal expands to a division sequence of about ten
+// instructions, which the gate/up and activation-gradient epilogues would run
+// 64 times per lane per tile.
+__device__ __forceinline__ float fast_sigmoid(float a) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+}
 
 // k-split parts: part_out (a helper) receives the tile's partial sums instead
 // of the outputs; part_in[0 .. n_in) (the owner's helpers) are added, in that
@@ -1212,21 +1220,19 @@ __device__ __forceinline__ void for_tasks_xcd_ranges(int32_t* cursors, int n, in
 }
 
 // Logical tile -> (row tile, column tile) over the planner's bands (a group's
-// row tiles in runs): bands in order, inside a band the
-// column tiles advance slowest.  Tiles running at the same time on an XCD
-// then belong to one or two experts, so they share weight columns as well as
-// token rows through L2.
-__device__ __forceinline__ void band_order_groups(int L, int nt_count, const int32_t* bands,
-                                                  int n_bands, int& tm, int& tn) {
-  int lo = 0, hi = n_bands;   // the band holding L: largest b with bands[b] * nt_count <= L
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (bands[mid] * nt_count <= L) lo = mid; else hi = mid;
-  }
-  const int first = bands[lo], rows = bands[lo + 1] - first;
-  const int rem = L - first * nt_count;
-  tn = rem / rows;
-  tm = first + (rem - tn * rows);
+// row tiles in runs): bands in order, inside a band the column tiles advance
+// slowest.  Tiles running at the same time on an XCD then belong to one or two
+// experts, so they share weight columns as well as token rows through L2.
+// Band b covers logical tiles [first_b * nt, (first_b + rows_b) * nt), so row
+// tile L / nt lies in the band holding L, and its band-table entry gives the
+// band with one load (a search over the band starts would be a chain of
+// dependent loads at the start of every tile).
+__device__ __forceinline__ void band_order_groups(int L, int nt_count, const int2* bands, int& tm,
+                                                  int& tn) {
+  const int2 b = bands[L / nt_count];
+  const int rem = L - b.x * nt_count;
+  tn = rem / b.y;
+  tm = b.x + (rem - tn * b.y);
 }
 
 // bf16 tile configurations per kind: BM, BN, waves along M, waves along N,

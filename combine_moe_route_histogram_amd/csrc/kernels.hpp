@@ -93,8 +93,8 @@ struct GemmArgs {
   const int32_t* offsets;  // [E+1] routed row ranges
   const int4* mtiles;      // per M-tile {group, first row (all-rows index), rows, 0}
   const int32_t* n_mtiles; // [0] valid entries in mtiles, [1] bands in `bands`, [2] in `bands2`
-  const int32_t* bands;    // [bands + 1] first M-tile of each band (the last entry is the M-tile count)
-  const int32_t* bands2;   // second band table over the same M-tiles (the one-launch backward's
+  const int2* bands;       // per M-tile: {first M-tile, M-tiles} of the band holding it
+  const int2* bands2;      // second band table over the same M-tiles (the one-launch backward's
                            // input-gradient phase), or null
   int mt_max;              // host bound on the number of M-tiles
   int wg_band;             // weight-gradient kinds: M tiles per band
@@ -179,18 +179,19 @@ constexpr int kMinTileM = 64;
 // cursors at `cursors` (cleared by the launch itself); f32: one workgroup per
 // tile.
 hipError_t launch_gemm(bool is_bf16, int kind, const GemmArgs& a, const Tuning& tu,
-                       int4* mtiles_ws, int32_t* n_mtiles_ws, int32_t* bands_ws, int32_t* cursors,
+                       int4* mtiles_ws, int32_t* n_mtiles_ws, int2* bands_ws, int32_t* cursors,
                        int workers, hipStream_t st);
 
 // Row-tile planner (one wave): table of bm-row tiles per group, the first
 // table index of every group (if first_tile), the band table (a group of at
-// most `small` row tiles is one band, a larger one runs of `big`) and, if
-// bands2, a second one with (small2, big2), and n_clear ints of `clear` set
-// to zero (flags and cursors of the fused kernels).
+// most `small` row tiles is one band, a larger one runs of `big`; per row
+// tile, the first row tile and the height of its band) and, if bands2, a
+// second one with (small2, big2), and n_clear ints of `clear` set to zero
+// (flags and cursors of the fused kernels).
 hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int bm, int small,
                        int big, int4* mtiles, int32_t* n_mtiles, int32_t* first_tile,
-                       int32_t* bands, int32_t* clear, int n_clear, hipStream_t st,
-                       int32_t* bands2 = nullptr, int small2 = 0, int big2 = 0);
+                       int2* bands, int32_t* clear, int n_clear, hipStream_t st,
+                       int2* bands2 = nullptr, int small2 = 0, int big2 = 0);
 
 // Fused persistent kernels (bf16).  ws_* are workspace sections.
 // Task cursors of a fused launch: [0] the x_perm copy (dispatch_ffn) or combine
@@ -205,8 +206,8 @@ struct FusedWs {
   int4* mtiles;
   int32_t* n_mtiles;
   int32_t* first_tile;  // [E + Ns]
-  int32_t* bands;       // [mt bound + 1]
-  int32_t* bands2;      // [mt bound + 1]
+  int2* bands;          // [mt bound]
+  int2* bands2;         // [mt bound]
   int32_t* flags;       // [mt bound]: done counters of the row tiles (ffn_combine)
   int32_t* cursor;      // [kFusedCursors], right after the flags
   int mt_bound;

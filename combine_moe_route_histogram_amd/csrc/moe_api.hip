@@ -52,8 +52,8 @@ Layout layout(const moe_dims* d) {
   L.chunk_base = off;   off = align_up(off + nchunk * d->E * 4);
   L.mtiles = off;       off = align_up(off + mt * 16);
   L.n_mtiles = off;     off = align_up(off + 16);
-  L.bands = off;        off = align_up(off + (mt + 1) * 4);
-  L.bands2 = off;       off = align_up(off + (mt + 1) * 4);
+  L.bands = off;        off = align_up(off + mt * 8);
+  L.bands2 = off;       off = align_up(off + mt * 8);
   L.first_tile = off;   off = align_up(off + (size_t)(d->E + d->n_shared) * 4);
   // row-tile counters, then the task cursors, then the split counters
   L.flags = off;        off = align_up(off + (mt + kFusedCursors + kXcds * kSplitWr) * 4);
@@ -244,7 +244,7 @@ int gemm(const moe_dims* d, int kind, const GemmArgs& a, void* ws, hipStream_t s
   MOE_TRY(current_cu_count(&workers));
   int32_t* cursors = ws_at<int32_t>(ws, L.flags) + L.mt_bound + 1;
   return hip_status(launch_gemm(d->dtype == MOE_BF16, kind, a, tuning_for(d), ws_at<int4>(ws, L.mtiles),
-                                ws_at<int32_t>(ws, L.n_mtiles), ws_at<int32_t>(ws, L.bands),
+                                ws_at<int32_t>(ws, L.n_mtiles), ws_at<int2>(ws, L.bands),
                                 cursors, workers, st),
                     what);
 }
@@ -278,8 +278,8 @@ int fused_ws(const moe_dims* d, void* ws, FusedWs* w) {
   w->mtiles = ws_at<int4>(ws, L.mtiles);
   w->n_mtiles = ws_at<int32_t>(ws, L.n_mtiles);
   w->first_tile = ws_at<int32_t>(ws, L.first_tile);
-  w->bands = ws_at<int32_t>(ws, L.bands);
-  w->bands2 = ws_at<int32_t>(ws, L.bands2);
+  w->bands = ws_at<int2>(ws, L.bands);
+  w->bands2 = ws_at<int2>(ws, L.bands2);
   w->flags = ws_at<int32_t>(ws, L.flags);
   w->cursor = w->flags + L.mt_bound;
   w->mt_bound = L.mt_bound;
