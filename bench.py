@@ -316,12 +316,13 @@ TUNE_CANDIDATES = {
     "band_wgrad_down": (2, 4, 8, 16),
     "combine_tokens": (8, 16, 32, 64),
     "copy_tokens": (16, 32, 64, 128),
+    "copy_in_tiles": (0, 1),
 }
 # the calls whose time each knob changes
 TUNE_CALLS = {
     "band_up": ("dispatch_ffn",), "band_act": ("ffn_bwd",), "small_group": ("dispatch_ffn", "ffn_bwd"),
     "band_wgrad_up": ("ffn_bwd",), "band_wgrad_down": ("ffn_bwd",), "combine_tokens": ("ffn_combine",),
-    "copy_tokens": ("dispatch_ffn",),
+    "copy_tokens": ("dispatch_ffn",), "copy_in_tiles": ("dispatch_ffn",),
 }
 
 

@@ -64,7 +64,7 @@ class Tuning(ctypes.Structure):
     _fields_ = [("band_up", ctypes.c_int32), ("band_act", ctypes.c_int32),
                 ("small_group", ctypes.c_int32), ("band_wgrad_up", ctypes.c_int32),
                 ("band_wgrad_down", ctypes.c_int32), ("combine_tokens", ctypes.c_int32),
-                ("copy_tokens", ctypes.c_int32)]
+                ("copy_tokens", ctypes.c_int32), ("copy_in_tiles", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: int(getattr(self, f)) for f, _ in self._fields_}

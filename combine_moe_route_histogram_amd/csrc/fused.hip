@@ -47,7 +47,9 @@ using UpCfg = BfPick<kUp>::C;
 using DownCfg = BfPick<kDown>::C;
 
 
-template <bool R>
+// kCopyInTiles: x_perm is written by the GEMM tiles from the gathered rows in
+// LDS (run_tile_bf16's kCopyA) instead of by copy tasks after the tiles.
+template <bool R, bool kCopyInTiles>
 __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
                                                                   const int32_t* __restrict__ slot,
                                                                   FusedWs w, int nt_count) {
@@ -62,8 +64,9 @@ __global__ __launch_bounds__(UpCfg::NT) void dispatch_ffn_kernel(GemmArgs g,
     int tm, tn;
     band_order_groups(tp.L, nt_count, w.bands, tm, tn);
     const TileDesc<uint16_t> d = decode_tile<uint16_t, kUp, C::BM, C::BN>(g, tm, tn);
-    run_tile_bf16<C, false, R>(g, d, ring, tp);
+    run_tile_bf16<C, false, R, kCopyInTiles>(g, d, ring, tp);
   }, g.perturb);
+  if constexpr (kCopyInTiles) return;
   // phase 2: the permuted copy x_perm (an output the backward reads), token
   // by token as the plain dispatch does it: each token row is read once and
   // written to its K slots (a copy by destination row would read every token
@@ -177,10 +180,14 @@ hipError_t launch_dispatch_ffn(const GemmArgs& a0, const Tuning& tu, const int32
                              w.mt_bound + kFusedCursors + kXcds * kSplitWr, st);
   if (e != hipSuccess) return e;
   const int nt = gemm_ntiles<kUp>(a.H, a.I, UpCfg::BN);
-  if (ragged_k(a.H, a.I, UpCfg::BK))
-    dispatch_ffn_kernel<true><<<w.workers, UpCfg::NT, 0, st>>>(a, slot, w, nt);
-  else
-    dispatch_ffn_kernel<false><<<w.workers, UpCfg::NT, 0, st>>>(a, slot, w, nt);
+  const bool rk = ragged_k(a.H, a.I, UpCfg::BK);
+  if (tu.copy_in_tiles) {
+    if (rk) dispatch_ffn_kernel<true, true><<<w.workers, UpCfg::NT, 0, st>>>(a, slot, w, nt);
+    else dispatch_ffn_kernel<false, true><<<w.workers, UpCfg::NT, 0, st>>>(a, slot, w, nt);
+  } else {
+    if (rk) dispatch_ffn_kernel<true, false><<<w.workers, UpCfg::NT, 0, st>>>(a, slot, w, nt);
+    else dispatch_ffn_kernel<false, false><<<w.workers, UpCfg::NT, 0, st>>>(a, slot, w, nt);
+  }
   return hipGetLastError();
 }
 

@@ -787,13 +787,34 @@ static inline hipError_t take_wait_error(uint32_t* out) {
 // end of k.
 inline bool ragged_k(int H, int I, int bk) { return (H % bk) != 0 || (I % bk) != 0; }
 
+// Copy of half of a k slice's A operand from LDS to global rows (the fused
+// dispatch+up writes the expert-contiguous rows x_perm this way): wave w
+// takes tile rows [32 w, 32 w + 32), lane l chunk l % 8 (8 k) of rows
+// l / 8 + 8 j, j = 2 half .. 2 half + 1.  Rows past m_valid and chunks past
+// k_valid (zero-filled in LDS) are not stored.
+template <class C>
+__device__ __forceinline__ void copy_a_half(const uint8_t* stage, uint16_t* dst, int64_t ld, int k0,
+                                            int k_valid, int m_valid, int wave, int lane, int half) {
+  constexpr int kCpr = C::BK / 8;
+  static_assert(!C::A_MN && C::BM == 32 * C::NW && kCpr == 8, "one 32-row block per wave");
+  const int c = lane % kCpr;
+#pragma unroll
+  for (int j = 2 * half; j < 2 * half + 2; ++j) {
+    const int r = 32 * wave + lane / kCpr + 8 * j;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + kc_off<C::BK>(r, c));
+    if (r < m_valid && c * 8 < k_valid) st16(dst + (int64_t)r * ld + k0 + c * 8, v);
+  }
+}
+
 // The whole tile: a ring of LDS k slices filled by direct loads, MFMA over
 // each slice with the next k step's fragments in flight, then the epilogue.
+// kCopyA (the fused dispatch+up): the first column tile of a routed row tile
+// also writes each A slice it has gathered from the token rows to x_perm.
 // A split tile's helper part stores its partial sums and publishes them; the
 // owner part (the last) waits for its helpers, adds their partials in part
 // order (a fixed order, so the bits do not depend on timing) and runs the
 // epilogue.
-template <class C, bool kCoherentY = false, bool kRaggedK = false>
+template <class C, bool kCoherentY = false, bool kRaggedK = false, bool kCopyA = false>
 __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
                               uint8_t* const (&stages)[4], const TaskPart& tp) {
   constexpr int MI = C::MI, NJ = C::NJ;
@@ -824,6 +845,9 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
   const int nk_all = two_seg ? 2 * nk_seg : (d.k_len + BK - 1) / BK;
   const int kb = parts > 1 ? (int)((int64_t)nk_all * part / parts) : 0;   // this part's slices
   const int nk = parts > 1 ? (int)((int64_t)nk_all * (part + 1) / parts) - kb : nk_all;
+  // kCopyA: gathered routed rows of the first column tile go to x_perm too
+  const bool copy_a = kCopyA && d.a_rows != nullptr && d.col0 == 0;
+  uint16_t* const xperm_rows = kCopyA ? static_cast<uint16_t*>(g.o_x_perm) + d.row0 * d.a_sm : nullptr;
   auto issue = [&](uint8_t* st, int kt) {   // kt: slice index within the part
     int ks = (kb + kt) * BK;                 // k of the slice within its segment
     int seg = 0;
@@ -952,6 +976,14 @@ __device__ void run_tile_bf16(const GemmArgs& g, const TileDesc<uint16_t>& d,
           else
             interleave_step<0, NA * NJ, kReads, 0>();
           __builtin_amdgcn_sched_barrier(0);
+          if constexpr (kCopyA) {
+            // the slice stays in its stage until the barrier that closes it
+            if (copy_a && ks < 2 && kt < nk) {
+              copy_a_half<C>(stages[i], xperm_rows, d.a_sm, (kb + kt) * BK, d.k_len - (kb + kt) * BK,
+                             d.m_valid, wave, lane, ks);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
         }
         wait_slices(min(S - 2, nk_pad - 2 - kt));
         lds_barrier();

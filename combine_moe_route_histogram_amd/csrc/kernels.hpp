@@ -81,6 +81,7 @@ struct Tuning {
   int band_wg_down;    // I blocks per band: dW2
   int combine_tokens;  // tokens per combine task of the fused down+combine
   int copy_tokens;     // tokens per x_perm copy task of the fused dispatch+up
+  int copy_in_tiles;   // 1: the fused dispatch+up writes x_perm from its GEMM tiles instead
 };
 
 // Fixed bands of the split kinds: groups of at most kSplitSmall row tiles are

@@ -129,7 +129,7 @@ struct DebugSettings {
   int wait_extra = 0;
   uint32_t perturb = 0;
   int fused_workers = 0;   // 0: one per CU
-  moe_tuning tune = {0, 0, 0, 0, 0, 0, 0};   // MOE_TUNE overrides (0: the shape's choice)
+  moe_tuning tune = {0, 0, 0, 0, 0, 0, 0, -1};   // MOE_TUNE overrides (0 / -1: the shape's choice)
 };
 std::mutex g_debug_mu;
 DebugSettings g_debug;
@@ -142,7 +142,7 @@ DebugSettings debug_settings() {
 // MOE_TUNE="key=value,...": schedule-knob overrides (keys as in moe_tuning).
 // Returns false for a malformed string or a value outside the knob's range.
 bool parse_tune(const char* e, moe_tuning* t) {
-  *t = moe_tuning{0, 0, 0, 0, 0, 0, 0};
+  *t = moe_tuning{0, 0, 0, 0, 0, 0, 0, -1};
   std::string s(e);
   size_t pos = 0;
   while (pos < s.size()) {
@@ -161,10 +161,15 @@ bool parse_tune(const char* e, moe_tuning* t) {
                   : key == "small_group" ? &t->small_group : key == "band_wgrad_up" ? &t->band_wgrad_up
                   : key == "band_wgrad_down" ? &t->band_wgrad_down
                   : key == "combine_tokens" ? &t->combine_tokens
-                  : key == "copy_tokens" ? &t->copy_tokens : nullptr;
+                  : key == "copy_tokens" ? &t->copy_tokens
+                  : key == "copy_in_tiles" ? &t->copy_in_tiles : nullptr;
     if (!slot) return false;
     const bool tokens = slot == &t->combine_tokens || slot == &t->copy_tokens;
-    if (v < 1 || v > (tokens ? kMaxTaskTokens : kMaxBand)) return false;
+    if (slot == &t->copy_in_tiles) {
+      if (v < 0 || v > 1) return false;
+    } else if (v < 1 || v > (tokens ? kMaxTaskTokens : kMaxBand)) {
+      return false;
+    }
     *slot = (int32_t)v;
   }
   return true;
@@ -204,10 +209,12 @@ Tuning tuning_for(const moe_dims* d) {
   if (o.band_wgrad_down) t.band_wgrad_down = o.band_wgrad_down;
   if (o.combine_tokens) t.combine_tokens = o.combine_tokens;
   if (o.copy_tokens) t.copy_tokens = o.copy_tokens;
+  if (o.copy_in_tiles >= 0) t.copy_in_tiles = o.copy_in_tiles;
   Tuning u;
   u.band_up = t.band_up; u.band_act = t.band_act; u.small_group = t.small_group;
   u.band_wg_up = t.band_wgrad_up; u.band_wg_down = t.band_wgrad_down;
   u.combine_tokens = t.combine_tokens; u.copy_tokens = t.copy_tokens;
+  u.copy_in_tiles = t.copy_in_tiles;
   return u;
 }
 
@@ -333,6 +340,7 @@ int moe_get_tuning(const moe_dims* d, moe_tuning* out) {
   out->band_up = u.band_up; out->band_act = u.band_act; out->small_group = u.small_group;
   out->band_wgrad_up = u.band_wg_up; out->band_wgrad_down = u.band_wg_down;
   out->combine_tokens = u.combine_tokens; out->copy_tokens = u.copy_tokens;
+  out->copy_in_tiles = u.copy_in_tiles;
   return MOE_OK;
 }
 

@@ -165,6 +165,10 @@ moe_tuning choose_tuning(int T, int H, int E, int K, int I, int Ns) {
   t.band_wgrad_down = 8;
   t.combine_tokens = 8;
   t.copy_tokens = 32;
+  // x_perm of the fused dispatch+up: copy tasks re-read the token rows x,
+  // cheap while x fits in half of the Infinity Cache; beyond that, writing it
+  // from the rows the tiles already gathered into LDS saves the HBM re-read
+  t.copy_in_tiles = (double)T * H * 2 > kMallBytes / 2 ? 1 : 0;
   return t;
 }
 

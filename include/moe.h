@@ -131,14 +131,18 @@ typedef struct {
   int32_t band_wgrad_down; /* I blocks per band of the dW2 GEMM                       */
   int32_t combine_tokens;  /* tokens per combine task of moe_ffn_combine              */
   int32_t copy_tokens;     /* tokens per x_perm copy task of moe_dispatch_ffn          */
+  int32_t copy_in_tiles;   /* 1: moe_dispatch_ffn writes x_perm from the gathered rows its
+                              GEMM tiles hold in LDS (no copy tasks), 0: copy tasks      */
 } moe_tuning;
 
 /* The knobs every call with these dims uses: the library's choice for the
  * shape (an analytical model of the operand traffic beyond L2 for the band
- * heights; measured defaults for the others), with any override from the
+ * heights; a cache-footprint rule for copy_in_tiles; measured defaults for
+ * the others), with any override from the
  * MOE_TUNE environment variable as moe_init read it ("key=value,..." with the
- * field names above; band heights 1..64, task sizes 1..1024; moe_init returns
- * MOE_EINVAL for anything else).  Errors: MOE_EINVAL (NULL), bad dims. */
+ * field names above; band heights 1..64, task sizes 1..1024, copy_in_tiles
+ * 0..1; moe_init returns MOE_EINVAL for anything else).  Errors: MOE_EINVAL
+ * (NULL), bad dims. */
 int moe_get_tuning(const moe_dims* d, moe_tuning* out);
 
 /* The band model's prediction behind moe_get_tuning: operand bytes fetched

@@ -222,6 +222,8 @@ def test_tuning_choice_is_valid_and_follows_the_traffic_model(lib):
         assert all(1 <= t[k] <= 64 for k in ("band_up", "band_act", "small_group", "band_wgrad_up",
                                               "band_wgrad_down")), (n, t)
         assert 1 <= t["combine_tokens"] <= 1024 and 1 <= t["copy_tokens"] <= 1024
+        # x_perm from the tiles only where the token rows do not fit in the cache
+        assert t["copy_in_tiles"] == (1 if c.T * c.H * 2 > 128 * 2**20 else 0), n
     assert _tuning(dims["longseq"])["band_up"] == 2
     assert _tuning(dims["longseq"])["band_act"] == 4
     assert _tuning(dims["dsv3"])["band_up"] == 4
@@ -242,7 +244,8 @@ def test_tuning_override_read_by_moe_init(lib, monkeypatch):
     assert t["band_up"] == 2 and t["combine_tokens"] == 64
     assert {k: v for k, v in t.items() if k not in ("band_up", "combine_tokens")} == \
         {k: v for k, v in base.items() if k not in ("band_up", "combine_tokens")}
-    for bad in ("band_up=0", "band_up=65", "copy_tokens=2000", "nope=3", "band_up", "band_up=x"):
+    for bad in ("band_up=0", "band_up=65", "copy_tokens=2000", "copy_in_tiles=2", "nope=3", "band_up",
+                "band_up=x"):
         monkeypatch.setenv("MOE_TUNE", bad)
         assert lib.moe_init(0) == 1, bad
     monkeypatch.delenv("MOE_TUNE")

@@ -27,6 +27,7 @@ KNOBS = {
     "band_wgrad_down": (1, 2, 4, 16),
     "combine_tokens": (1, 7, 16, 64),
     "copy_tokens": (1, 5, 128),
+    "copy_in_tiles": (0, 1),
 }
 OUTS = ("x_perm", "ab", "h", "y", "out", "dy", "dtopk_w", "dab", "dx_rows", "dx", "dlogits",
         "dw1", "dw3", "dw2", "dws1", "dws3", "dws2")
