@@ -19,23 +19,22 @@ namespace moe {
 // (group_bands); bands[tm] = {first row tile, row tiles} of the band holding
 // row tile tm (so a worker finds a tile's band with one load), n_mtiles[1] =
 // number of bands; bands2 (if not null) likewise with small2, big2 and
-// n_mtiles[2].  One wave: each lane owns a contiguous run of groups, wave
-// scans give every lane its first table indices.
-__global__ __launch_bounds__(64) void plan_mtiles_kernel(const int32_t* __restrict__ offsets, int E,
-                                                         int Ns, int T, int R, int bm, int small,
-                                                         int big, int4* __restrict__ mtiles,
-                                                         int32_t* __restrict__ n_mtiles,
-                                                         int32_t* __restrict__ first_tile,
-                                                         int2* __restrict__ bands,
-                                                         int2* __restrict__ bands2, int small2,
-                                                         int big2, int32_t* __restrict__ clear,
-                                                         int n_clear) {
+// n_mtiles[2].  Wave 0 places the groups: each lane owns a contiguous run of
+// groups, and wave scans give each group its first table index (kept in LDS).
+// Then every thread writes table entries: entry i's group is the last one
+// whose first index is <= i (a binary search in LDS).
+constexpr int kPlanThreads = 256;
+__global__ __launch_bounds__(kPlanThreads) void plan_mtiles_kernel(
+    const int32_t* __restrict__ offsets, int E, int Ns, int T, int R, int bm, int small, int big,
+    int4* __restrict__ mtiles, int32_t* __restrict__ n_mtiles, int32_t* __restrict__ first_tile,
+    int2* __restrict__ bands, int2* __restrict__ bands2, int small2, int big2,
+    int32_t* __restrict__ clear, int n_clear) {
   __shared__ int off_s[kMaxExperts + 1];
-  const int lane = threadIdx.x;
+  __shared__ int first_s[kMaxExperts + kMaxShared + 1];   // per group, then the entry count
+  const int tid = threadIdx.x;
   const int G = E + Ns;
-  const int per = (G + kWave - 1) / kWave;
-  const int g_begin = min(G, lane * per), g_end = min(G, g_begin + per);
-  for (int e = lane; e <= E; e += kWave) off_s[e] = offsets[e];   // all loads in flight at once
+  for (int e = tid; e <= E; e += kPlanThreads) off_s[e] = offsets[e];   // all loads in flight at once
+  for (int i = tid; i < n_clear; i += kPlanThreads) clear[i] = 0;
   __syncthreads();
   auto group_rows = [&](int grp, int& row0, int& rows) {
     if (grp < E) {
@@ -46,62 +45,74 @@ __global__ __launch_bounds__(64) void plan_mtiles_kernel(const int32_t* __restri
       rows = T;
     }
   };
-  int mine = 0, mine_b = 0, mine_b2 = 0;
-  for (int grp = g_begin; grp < g_end; ++grp) {
-    int row0, rows;
-    group_rows(grp, row0, rows);
-    const int mt = (rows + bm - 1) / bm;
-    mine += mt;
-    mine_b += group_bands(mt, small, big);
-    if (bands2) mine_b2 += group_bands(mt, small2, big2);
-  }
-  int incl = mine, incl_b = mine_b, incl_b2 = mine_b2;
+  if (tid < kWave) {
+    const int lane = tid;
+    const int per = (G + kWave - 1) / kWave;
+    const int g_begin = min(G, lane * per), g_end = min(G, g_begin + per);
+    int mine = 0, mine_b = 0, mine_b2 = 0;
+    for (int grp = g_begin; grp < g_end; ++grp) {
+      int row0, rows;
+      group_rows(grp, row0, rows);
+      const int mt = (rows + bm - 1) / bm;
+      mine += mt;
+      mine_b += group_bands(mt, small, big);
+      if (bands2) mine_b2 += group_bands(mt, small2, big2);
+    }
+    int incl = mine, incl_b = mine_b, incl_b2 = mine_b2;
 #pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(incl, o, kWave);
-    const int yb = __shfl_up(incl_b, o, kWave);
-    const int yb2 = __shfl_up(incl_b2, o, kWave);
-    if (lane >= o) {
-      incl += y;
-      incl_b += yb;
-      incl_b2 += yb2;
-    }
-  }
-  int idx = incl - mine, bidx = incl_b - mine_b, bidx2 = incl_b2 - mine_b2;
-  for (int grp = g_begin; grp < g_end; ++grp) {
-    int row0, rows;
-    group_rows(grp, row0, rows);
-    if (first_tile) first_tile[grp] = idx;
-    const int mt = (rows + bm - 1) / bm;
-    const int step = mt <= small ? small : big;
-    for (int c = 0; c < mt; c += step) {
-      const int h = min(step, mt - c);
-      for (int j = 0; j < h; ++j) bands[idx + c + j] = make_int2(idx + c, h);
-      ++bidx;
-    }
-    if (bands2) {
-      const int step2 = mt <= small2 ? small2 : big2;
-      for (int c = 0; c < mt; c += step2) {
-        const int h = min(step2, mt - c);
-        for (int j = 0; j < h; ++j) bands2[idx + c + j] = make_int2(idx + c, h);
-        ++bidx2;
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(incl, o, kWave);
+      const int yb = __shfl_up(incl_b, o, kWave);
+      const int yb2 = __shfl_up(incl_b2, o, kWave);
+      if (lane >= o) {
+        incl += y;
+        incl_b += yb;
+        incl_b2 += yb2;
       }
     }
-    for (int r = 0; r < rows; r += bm) mtiles[idx++] = make_int4(grp, row0 + r, min(bm, rows - r), 0);
+    int idx = incl - mine;
+    for (int grp = g_begin; grp < g_end; ++grp) {
+      int row0, rows;
+      group_rows(grp, row0, rows);
+      first_s[grp] = idx;
+      if (first_tile) first_tile[grp] = idx;
+      idx += (rows + bm - 1) / bm;
+    }
+    if (lane == kWave - 1) {
+      first_s[G] = incl;
+      n_mtiles[0] = incl;
+      n_mtiles[1] = incl_b;
+      if (bands2) n_mtiles[2] = incl_b2;
+    }
   }
-  if (lane == kWave - 1) {
-    n_mtiles[0] = incl;
-    n_mtiles[1] = bidx;
-    if (bands2) n_mtiles[2] = bidx2;
+  __syncthreads();
+  const int n_mt = first_s[G];
+  for (int i = tid; i < n_mt; i += kPlanThreads) {
+    int lo = 0, hi = G;   // first_s[lo] <= i < first_s[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (first_s[mid] <= i) lo = mid; else hi = mid;
+    }
+    const int f = first_s[lo], mt = first_s[lo + 1] - f, j = i - f;
+    int row0, rows;
+    group_rows(lo, row0, rows);
+    mtiles[i] = make_int4(lo, row0 + j * bm, min(bm, rows - j * bm), 0);
+    const int step = mt <= small ? small : big;
+    const int c = j / step * step;
+    bands[i] = make_int2(f + c, min(step, mt - c));
+    if (bands2) {
+      const int step2 = mt <= small2 ? small2 : big2;
+      const int c2 = j / step2 * step2;
+      bands2[i] = make_int2(f + c2, min(step2, mt - c2));
+    }
   }
-  for (int i = lane; i < n_clear; i += kWave) clear[i] = 0;
 }
 
 hipError_t launch_plan(const int32_t* offsets, int E, int Ns, int T, int R, int bm, int small,
                        int big, int4* mtiles, int32_t* n_mtiles, int32_t* first_tile,
                        int2* bands, int32_t* clear, int n_clear, hipStream_t st,
                        int2* bands2, int small2, int big2) {
-  plan_mtiles_kernel<<<1, 64, 0, st>>>(offsets, E, Ns, T, R, bm, small, big, mtiles, n_mtiles,
+  plan_mtiles_kernel<<<1, kPlanThreads, 0, st>>>(offsets, E, Ns, T, R, bm, small, big, mtiles, n_mtiles,
                                        first_tile, bands, bands2, small2, big2, clear, n_clear);
   return hipGetLastError();
 }

@@ -14,6 +14,7 @@ constexpr int kChunkTokens = 64;
 // Largest number of routed experts (the routing kernels keep one LDS word per
 // expert; the planner stages E + 1 offsets in LDS).
 constexpr int kMaxExperts = 256;
+constexpr int kMaxShared = 8;      // shared experts per layer at most
 
 inline int route_nchunk(int T) { return (T + kChunkTokens - 1) / kChunkTokens; }
 

@@ -81,8 +81,8 @@ int check_dims(const moe_dims* d) {
     return fail(MOE_EUNSUPPORTED, "H must be a positive multiple of 8 (got %d)", d->H);
   if (d->I <= 0 || d->I % 8)
     return fail(MOE_EUNSUPPORTED, "I must be a positive multiple of 8 (got %d)", d->I);
-  if (d->n_shared < 0 || d->n_shared > 8)
-    return fail(MOE_EUNSUPPORTED, "n_shared must be in [0, 8] (got %d)", d->n_shared);
+  if (d->n_shared < 0 || d->n_shared > kMaxShared)
+    return fail(MOE_EUNSUPPORTED, "n_shared must be in [0, %d] (got %d)", kMaxShared, d->n_shared);
   if (d->n_shared > 0 && d->I_shared != d->I)
     return fail(MOE_EUNSUPPORTED,
                 "shared experts must have the routed experts' intermediate dim (I_shared=%d, I=%d)",

@@ -43,6 +43,61 @@ __device__ __forceinline__ float route_key_logit(uint64_t key) {
 
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
+// One lane per token (E <= EMAX <= 32, K <= kLaneMaxK): the token's logits sit
+// in the lane's registers and each of the K picks scans them, the first
+// maximum winning (the lowest expert id among equal logits), so a wave routes
+// 64 tokens without cross-lane traffic.  Same keys, picks, order and weight
+// arithmetic as the group kernel below, hence the same bits.
+constexpr int kLaneMaxK = 8;
+template <int EMAX>
+__global__ __launch_bounds__(64) void route_topk_lane_kernel(const float* __restrict__ logits, int T,
+                                                             int E, int K, int32_t* __restrict__ topk_idx,
+                                                             float* __restrict__ topk_w) {
+  const int t = blockIdx.x * kWave + threadIdx.x;
+  if (t >= T) return;
+  const float* row = logits + (int64_t)t * E;
+  uint32_t key[EMAX];
+  if (E == EMAX) {   // whole row: 16-byte loads (rows are 16-byte aligned)
+#pragma unroll
+    for (int i = 0; i < EMAX / 4; ++i) {
+      const float4 v = reinterpret_cast<const float4*>(row)[i];
+      key[4 * i] = route_ord(v.x);
+      key[4 * i + 1] = route_ord(v.y);
+      key[4 * i + 2] = route_ord(v.z);
+      key[4 * i + 3] = route_ord(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) key[e] = e < E ? route_ord(row[e]) : 0u;   // 0: none
+  }
+  float l0 = 0.f, zsum = 0.f, pl[kLaneMaxK];
+#pragma unroll
+  for (int k = 0; k < kLaneMaxK; ++k) {
+    if (k < K) {
+      uint32_t best = key[0];
+      int be = 0;
+#pragma unroll
+      for (int e = 1; e < EMAX; ++e) {
+        if (key[e] > best) {
+          best = key[e];
+          be = e;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e)
+        if (e == be) key[e] = 0u;   // an expert is picked once
+      const float l = route_ord_logit(best);
+      if (k == 0) l0 = l;
+      zsum += expf(l - l0);
+      pl[k] = l;
+      topk_idx[(int64_t)t * K + k] = be;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kLaneMaxK; ++k)
+    if (k < K) topk_w[(int64_t)t * K + k] = expf(pl[k] - l0) / zsum;
+}
+
 // One group of G lanes per token (G = min(64, next pow2 >= E)); each lane owns
 // up to 4 experts (e = lane + i*G).  K rounds of a group-wide max over the
 // keys pick the experts in descending order.  Block = 256 threads = 4 waves,
@@ -244,7 +299,18 @@ hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* topk_
   while (g < E && g < 64) g <<= 1;
   const int per_block = 4 * (kWave / g);
   const dim3 grid((T + per_block - 1) / per_block), block(256);
+  const int lane_grid = (T + kWave - 1) / kWave;
+  if (E <= 32 && K <= kLaneMaxK) g = E <= 8 ? -8 : E <= 16 ? -16 : -32;   // the lane kernel
   switch (g) {
+    case -8:
+      route_topk_lane_kernel<8><<<lane_grid, kWave, 0, st>>>(logits, T, E, K, topk_idx, topk_w);
+      break;
+    case -16:
+      route_topk_lane_kernel<16><<<lane_grid, kWave, 0, st>>>(logits, T, E, K, topk_idx, topk_w);
+      break;
+    case -32:
+      route_topk_lane_kernel<32><<<lane_grid, kWave, 0, st>>>(logits, T, E, K, topk_idx, topk_w);
+      break;
 #define MOE_ROUTE_CASE(G)                                                                      \
   case G:                                                                                      \
     route_topk_kernel<G><<<grid, block, 0, st>>>(logits, T, E, K, topk_idx, topk_w);           \

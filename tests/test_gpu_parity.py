@@ -132,6 +132,43 @@ ROUTE_CASES = [
 ]
 
 
+LANE_CASES = [(131072, 32, 4, "gauss"), (5000, 8, 2, "ties"), (3001, 16, 8, "ties"),
+              (777, 32, 8, "equal"), (129, 20, 3, "gauss"), (64, 5, 5, "ties")]
+
+
+@pytest.mark.parametrize("case", LANE_CASES, ids=[str(c) for c in LANE_CASES])
+def test_route_lane_and_group_topk_agree(case):
+    """E <= 32 and K <= 8 take the top-k with one lane per token; the same
+    logits padded to 33 experts with -inf columns (never picked) take the
+    group kernel.  The picks must match the oracle and the two kernels must
+    give the same bits, weights included."""
+    from combine_moe_route_histogram_amd import layer as L
+    T, E, K, kind = case
+    g = np.random.default_rng(T + 31 * E + K)
+    if kind == "gauss":
+        logits = g.standard_normal((T, E)).astype(np.float32)
+    elif kind == "ties":
+        logits = g.integers(-1, 2, size=(T, E)).astype(np.float32)
+        logits[g.random((T, E)) < 0.25] = -0.0
+    else:
+        logits = np.full((T, E), 0.5, np.float32)
+    padded = np.full((T, 33), -np.inf, np.float32)
+    padded[:, :E] = logits
+    out = []
+    for lg in (logits, padded):
+        d = L.make_dims(T, 64, lg.shape[1], K, 64, 0, "bf16")
+        b = L.Buffers(d, backward=False)
+        print(f"case lane/group top-k T={T} E={lg.shape[1]} K={K} {kind}", flush=True)
+        L.route(b, {"logits": torch.from_numpy(lg).cuda()})
+        torch.cuda.synchronize()
+        out.append((host(b.topk_idx), host(b.topk_w)))
+    idx, w = O.route(logits, K)
+    assert np.array_equal(out[0][0], idx)
+    assert np.array_equal(out[0][0], out[1][0])
+    assert np.array_equal(out[0][1].view(np.uint32), out[1][1].view(np.uint32))
+    assert np.max(np.abs(out[0][1] - w)) <= 1e-6
+
+
 @pytest.mark.parametrize("case", ROUTE_CASES, ids=[str(c) for c in ROUTE_CASES])
 def test_route_bit_exact(case):
     from combine_moe_route_histogram_amd import layer as L
