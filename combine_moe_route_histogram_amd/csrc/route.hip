@@ -47,14 +47,15 @@ __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > 
 // in the lane's registers and each of the K picks scans them, the first
 // maximum winning (the lowest expert id among equal logits), so a wave routes
 // 64 tokens without cross-lane traffic.  Same keys, picks, order and weight
-// arithmetic as the group kernel below, hence the same bits.
+// arithmetic as the group kernel below, hence the same bits.  A wave's tokens
+// are one routing chunk, so it also writes the chunk's expert histogram
+// (chunk_counts[c][e], as chunk_hist_kernel does).
 constexpr int kLaneMaxK = 8;
+static_assert(kChunkTokens == kWave, "one wave of the lane kernel is one routing chunk");
 template <int EMAX>
-__global__ __launch_bounds__(64) void route_topk_lane_kernel(const float* __restrict__ logits, int T,
-                                                             int E, int K, int32_t* __restrict__ topk_idx,
-                                                             float* __restrict__ topk_w) {
-  const int t = blockIdx.x * kWave + threadIdx.x;
-  if (t >= T) return;
+__device__ __forceinline__ void route_lane_token(const float* __restrict__ logits, int t, int E, int K,
+                                                 int32_t* __restrict__ topk_idx,
+                                                 float* __restrict__ topk_w, int* hist) {
   const float* row = logits + (int64_t)t * E;
   uint32_t key[EMAX];
   if (E == EMAX) {   // whole row: 16-byte loads (rows are 16-byte aligned)
@@ -91,11 +92,27 @@ __global__ __launch_bounds__(64) void route_topk_lane_kernel(const float* __rest
       zsum += expf(l - l0);
       pl[k] = l;
       topk_idx[(int64_t)t * K + k] = be;
+      atomicAdd(&hist[be], 1);
     }
   }
 #pragma unroll
   for (int k = 0; k < kLaneMaxK; ++k)
     if (k < K) topk_w[(int64_t)t * K + k] = expf(pl[k] - l0) / zsum;
+}
+
+template <int EMAX>
+__global__ __launch_bounds__(64) void route_topk_lane_kernel(const float* __restrict__ logits, int T,
+                                                             int E, int K, int32_t* __restrict__ topk_idx,
+                                                             float* __restrict__ topk_w,
+                                                             int32_t* __restrict__ chunk_counts) {
+  __shared__ int hist[EMAX];
+  const int lane = threadIdx.x, c = blockIdx.x;
+  const int t = c * kWave + lane;
+  if (lane < EMAX) hist[lane] = 0;
+  __syncthreads();
+  if (t < T) route_lane_token<EMAX>(logits, t, E, K, topk_idx, topk_w, hist);
+  __syncthreads();
+  if (lane < E) chunk_counts[(int64_t)c * E + lane] = hist[lane];
 }
 
 // One group of G lanes per token (G = min(64, next pow2 >= E)); each lane owns
@@ -303,13 +320,16 @@ hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* topk_
   if (E <= 32 && K <= kLaneMaxK) g = E <= 8 ? -8 : E <= 16 ? -16 : -32;   // the lane kernel
   switch (g) {
     case -8:
-      route_topk_lane_kernel<8><<<lane_grid, kWave, 0, st>>>(logits, T, E, K, topk_idx, topk_w);
+      route_topk_lane_kernel<8><<<lane_grid, kWave, 0, st>>>(logits, T, E, K, topk_idx, topk_w,
+                                                               chunk_counts);
       break;
     case -16:
-      route_topk_lane_kernel<16><<<lane_grid, kWave, 0, st>>>(logits, T, E, K, topk_idx, topk_w);
+      route_topk_lane_kernel<16><<<lane_grid, kWave, 0, st>>>(logits, T, E, K, topk_idx, topk_w,
+                                                               chunk_counts);
       break;
     case -32:
-      route_topk_lane_kernel<32><<<lane_grid, kWave, 0, st>>>(logits, T, E, K, topk_idx, topk_w);
+      route_topk_lane_kernel<32><<<lane_grid, kWave, 0, st>>>(logits, T, E, K, topk_idx, topk_w,
+                                                               chunk_counts);
       break;
 #define MOE_ROUTE_CASE(G)                                                                      \
   case G:                                                                                      \
@@ -326,7 +346,7 @@ hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* topk_
     default:
       return hipErrorInvalidValue;
   }
-  chunk_hist_kernel<<<nchunk, 64, 0, st>>>(topk_idx, nullptr, T, E, K, chunk_counts);
+  if (g > 0) chunk_hist_kernel<<<nchunk, 64, 0, st>>>(topk_idx, nullptr, T, E, K, chunk_counts);
   route_chunk_scan_kernel<<<E, 256, 0, st>>>(chunk_counts, nchunk, E, chunk_base, counts);
   route_slot_kernel<<<nchunk, 64, 0, st>>>(topk_idx, counts, chunk_base, nullptr, T, E, K, offsets,
                                            slot, slot_src);
