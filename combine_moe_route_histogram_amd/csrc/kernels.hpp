@@ -184,7 +184,7 @@ hipError_t launch_gemm(bool is_bf16, int kind, const GemmArgs& a, const Tuning& 
                        int4* mtiles_ws, int32_t* n_mtiles_ws, int2* bands_ws, int32_t* cursors,
                        int workers, hipStream_t st);
 
-// Row-tile planner (one wave): table of bm-row tiles per group, the first
+// Row-tile planner (one block): table of bm-row tiles per group, the first
 // table index of every group (if first_tile), the band table (a group of at
 // most `small` row tiles is one band, a larger one runs of `big`; per row
 // tile, the first row tile and the height of its band) and, if bands2, a
