@@ -499,6 +499,17 @@ __device__ __forceinline__ void st_bf16x4(void* p, const float* v) {
   w[1] = pack_bf16x2(v[2], v[3]);
   *reinterpret_cast<u32x2*>(p) = w;
 }
+// The same with a non-temporal store: for the activation gradient's da | db,
+// which no tile of the launch reads back soon and which exceed the Infinity
+// Cache at the long-sequence size (one-launch backward 16.08 -> 16.02 ms
+// there, equal at the Mixtral-like size; non-temporal a | b, h or dx_rows
+// stores were slower or equal).
+__device__ __forceinline__ void st_bf16x4_nt(void* p, const float* v) {
+  u32x2 w;
+  w[0] = pack_bf16x2(v[0], v[1]);
+  w[1] = pack_bf16x2(v[2], v[3]);
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
+}
 // Stores that other workgroups of the same launch read (the down
 // projection's output rows, which the fused combine reads, and split-k
 // partial sums): relaxed agent-scope atomic stores.  Each is coherent at
@@ -694,8 +705,8 @@ __device__ __forceinline__ void epilogue_bf16(const GemmArgs& g, const TileDesc<
                 db[e] = v[e] * a[e] * sg;
               }
               uint16_t* dab = static_cast<uint16_t*>(g.o_dab) + row * 2 * I;
-              st_bf16x4(dab + col, da);
-              st_bf16x4(dab + I + col, db);
+              st_bf16x4_nt(dab + col, da);
+              st_bf16x4_nt(dab + I + col, db);
             } else {  // kWgDown
               const bool shared = d.group >= g.E;
               const int64_t e = shared ? d.group - g.E : d.group;
